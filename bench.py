@@ -1,0 +1,271 @@
+"""Benchmark of the CSA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+csa_index_scores -> csa_topk -> csa_decode_attn (or csa_prefill_attn).
+Default workload: batched CSA decode (64 sequences, 4096..32768-token
+contexts, paged FP8 cache with a shuffled page table, 128 heads x 512-d
+latent, indexer 64 x 128, top-k 512, window 128).
+
+Output: one JSON line with the throughput, a roofline object for the
+dominant kernel (algorithmic bytes or FLOPs per launch / the kernel's
+average duration measured with HIP events on its stream over the timed
+region), and the FP64 CPU oracle timed on a bounded sample of the same
+workload.  Inputs are rotated over several device copies so that every step
+reads HBM, not the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BASE_METRIC = "CSA decode queries/s (indexer+top-k+FMHA); % of HBM & FP8-MFMA roofline"
+PREFILL_METRIC = "CSA prefill tokens/s (indexer+top-k+FMHA); % of HBM & FP8-MFMA roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+WORKLOADS = {
+    "c1": "single-sequence CSA decode: 1 query, 8192-token context (2048 entries, 2047 visible), 128 heads x "
+          "(448 FP8 + 64 BF16), indexer 64x128 FP8, top-k 512, window 128",
+    "c2": "batched CSA decode: 64 sequences, contexts uniform over multiples of 4 in [4096, 32768], page 64 "
+          "with shuffled page table, 128 heads x (448 FP8 + 64 BF16), indexer 64x128 FP8, top-k 512, window 128",
+    "c3_csa": "long-context CSA decode: 4 sequences x 524288 tokens (131072 entries), top-k 512, window 128",
+    "c3_hca": "long-context HCA decode: 4 sequences x 524288 tokens, m'=128 (4096 entries, all visible ones "
+              "attended), window 128, no indexer",
+    "c4": "CSA prefill chunk: 2048 queries at positions 63488..65535 of a 65536-token context (16384 entries), "
+          "top-k 512, window 128",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle's CPU time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=0, help="device copies of the inputs (0 = enough for 1 GB)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- accounting
+def accounting(wl):
+    """Algorithmic bytes and FLOPs per launch of each step: only what the
+    method must move (visible index keys once, q_idx, w, scores written and
+    read back, selected + window latent rows once per query, q and o)."""
+    import numpy as np
+    s = wl.spec
+    T = wl.T
+    pos = wl.q_pos.astype(np.int64)
+    seq = wl.q_seq.astype(np.int64)
+    nv = np.minimum(pos // s.m, wl.n_comp[seq].astype(np.int64))
+    n_sel = np.minimum(nv, s.k) if wl.q_idx is not None else nv
+    if s.kind == "decode":
+        lo = np.maximum(pos - s.W + 1, 0)
+        n_win = np.array([int(((wl.swa_pos[b] >= lo[t]) & (wl.swa_pos[b] <= pos[t])).sum())
+                          for t, b in enumerate(seq)])
+    else:
+        lo = np.maximum(np.maximum(pos - s.W + 1, 0), wl.swa_first_pos)
+        hi = np.minimum(pos, wl.swa_first_pos + wl.swa_len - 1)
+        n_win = np.maximum(hi - lo + 1, 0)
+    row = s.D_nope + 2 * s.D_rope
+    acc = {}
+    if wl.q_idx is not None:
+        if s.kind == "decode":
+            key_bytes = int(nv.sum()) * s.D_I
+        else:
+            key_bytes = int(nv.max()) * s.D_I     # one sequence: every key is read once per chunk
+        acc["index_scores"] = dict(
+            bytes=key_bytes + T * s.H_I * (s.D_I + 4) + int(nv.sum()) * 4 + T * 4,
+            flops=2.0 * s.H_I * s.D_I * float(nv.sum()))
+        acc["topk"] = dict(bytes=int(nv.sum()) * 4 + T * s.k * 4 + T * 4, flops=0.0)
+    keys = n_sel + n_win
+    if s.kind == "decode":
+        lat_bytes = int(keys.sum()) * row
+    else:
+        lat_bytes = int(nv.max()) * row + wl.swa_len * row   # union of rows, counted once
+    attn = "decode_attn" if s.kind == "decode" else "prefill_attn"
+    acc[attn] = dict(
+        bytes=lat_bytes + T * s.H * s.D * 2 * 2 + T * s.H * 4 + (T * s.k * 4 if wl.q_idx is not None else 0),
+        flops=4.0 * s.H * s.D * float(keys.sum()))
+    return acc
+
+
+def roofline_entry(name, a, ms):
+    sec = ms * 1e-3
+    intensity = a["flops"] / max(a["bytes"], 1)
+    gbs = a["bytes"] / sec / 1e9
+    tfl = a["flops"] / sec / 1e12
+    if a["flops"] > 0 and intensity >= RIDGE:
+        return dict(bound="mfma", achieved=round(tfl, 2), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                    frac=round(tfl / PEAK_FP8_TFLOPS, 4))
+    return dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(gbs / PEAK_HBM_GBS, 4))
+
+
+def kernel_source_sha(name):
+    src = {"index_scores": "index_scores.hip", "topk": "topk.hip", "decode_attn": "attn.hip",
+           "prefill_attn": "attn.hip"}[name]
+    h = hashlib.sha256()
+    for f in (src, "csa_device.h", "csa_internal.h"):
+        with open(os.path.join(ROOT, "sparse_compressed_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, name):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data.get(workload, {}).get(name)
+        if ent and ent.get("source_sha") == kernel_source_sha(name):
+            return int(ent["hbm_bytes_per_launch"])
+    except (ValueError, KeyError, OSError):
+        return None
+    return None
+
+
+# --------------------------------------------------------------- CPU oracle leg
+def cpu_baseline(wl, gpu_res, seconds, is_prefill):
+    import numpy as np
+    import oracle
+    from tests import parity as P
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - informational only
+        cores = len(os.sched_getaffinity(0))
+    order = list(range(wl.T))
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    done = []
+    errs = []
+    t0 = time.perf_counter()
+    for t in order:
+        res = oracle.run_decode_path(wl, queries=[t]) if wl.q_idx is not None else None
+        if res is not None:
+            o_ref, l_ref = P.reference_attention_on(wl, t, gpu_res["topk"][t])
+        else:
+            o_ref, l_ref = oracle.run_attention(wl, None, queries=[t])
+            o_ref, l_ref = o_ref[0], l_ref[0]
+        done.append(t)
+        errs.append(P.check_attention(gpu_res["o"][t], gpu_res["lse"][t], o_ref, l_ref))
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    unit = "tokens/s" if is_prefill else "queries/s"
+    return dict(value=round(len(done) / el, 3), unit=unit, cores=int(cores), kind="oracle",
+                sample=f"{len(done)} of {wl.T} queries (random order, seed 0), FP64 NumPy oracle, "
+                       f"{el:.1f} s; its outputs also checked the GPU's: max|o-ref| "
+                       f"{max(e[0] for e in errs):.2e}, min per-head cos {min(e[1] for e in errs):.6f}")
+
+
+# --------------------------------------------------------------- main
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the CSA path here is a single-GPU build with no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import csa_inputs as ci
+    import sparse_compressed_attention_amd as csa
+    from csa_inputs.device import to_device, make_path
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    csa.load_library()
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    name = args.workload
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    wl = ci.make_config(name)
+    acc = accounting(wl)
+    d0 = to_device(wl, dev)
+    footprint = sum(t.numel() * t.element_size() for t in vars(d0).values() if isinstance(t, torch.Tensor))
+    copies = args.copies or int(min(256, max(2, math.ceil((1 << 30) / max(footprint, 1)))))
+    paths = [make_path(d0)] + [make_path(to_device(wl, dev)) for _ in range(copies - 1)]
+    del d0
+    stages = paths[0].stage_names
+    stream = torch.cuda.current_stream()
+    st = csa._stream(stream)
+    print(f"[bench] {copies} input copies of {footprint / 2**20:.1f} MiB; stages {stages}", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        paths[i % copies].run(st)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        p = paths[i % copies]
+        e = evs[i]
+        for j in range(len(stages)):
+            e[j].record(stream)
+            p.run_stage(j, st)
+        e[-1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_stage = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K for j in range(len(stages))]
+    gpu_step = sum(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K)) / K
+    ms_per_step = wall * 1e3 / K
+    n_items = wl.T
+    value = n_items / (ms_per_step * 1e-3)
+
+    kernels = {}
+    for nm, ms in zip(stages, per_stage):
+        a = acc[nm]
+        kernels[nm] = dict(ms=round(ms, 5), bytes=int(a["bytes"]), flops=a["flops"],
+                           GBps=round(a["bytes"] / (ms * 1e-3) / 1e9, 1),
+                           TFLOPs=round(a["flops"] / (ms * 1e-3) / 1e12, 2))
+    dom = max(range(len(stages)), key=lambda j: per_stage[j])
+    dom_name = stages[dom]
+    roof = roofline_entry(dom_name, acc[dom_name], per_stage[dom])
+    roof["kernel"] = dom_name
+    roof["traffic"] = measured_traffic(name, dom_name)
+
+    out = dict(
+        metric=PREFILL_METRIC if wl.spec.kind == "prefill" else BASE_METRIC,
+        value=round(value, 2),
+        unit="tokens/s" if wl.spec.kind == "prefill" else "queries/s",
+        n_gpus=1, steps=K, warmup=args.warmup, ms_per_step=round(ms_per_step, 5),
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="fp8", data="synthetic",
+        config=dict(workload=f"{name}: {WORKLOADS[name]}", queries_per_step=n_items, input_copies=copies,
+                    gpu_ms_per_step=round(gpu_step, 5)),
+        roofline=roof,
+        kernels=kernels,
+    )
+    if not args.no_cpu_baseline:
+        last = paths[(K - 1) % copies]
+        res = dict(o=last.out.float().cpu().numpy().astype(np.float64),
+                   lse=last.lse.cpu().numpy().astype(np.float64))
+        if getattr(last, "topk", None) is not None:
+            res["topk"] = last.topk.cpu().numpy()
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, res, args.cpu_seconds, wl.spec.kind == "prefill")
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,75 @@
+// Parameter blocks and launchers shared by the C ABI (csa_abi.cpp) and the
+// kernels.  Host-validated before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct IndexParams {
+  const uint8_t* q_idx;
+  const float* w;
+  const uint8_t* k_idx;
+  const int32_t* page_table;
+  const int32_t* n_comp;
+  const int32_t* q_pos;
+  const int32_t* q_seq;
+  float* scores;
+  int32_t* n_visible;
+  int64_t ld;
+  float qk_scale;     // q_idx_scale * k_idx_scale
+  int num_pages, page_size, max_pages, B;
+  int T, H_I, D_I, ratio_m;
+  int chunk, n_chunks;
+};
+hipError_t launch_index_scores(const IndexParams& p, hipStream_t stream);
+int index_chunk_entries();
+
+struct TopkParams {
+  const float* scores;
+  const int32_t* n_visible;
+  int32_t* out;
+  uint32_t* cand_key;   // [T][n_chunks][k] (multi-chunk rows only)
+  int32_t* cand_idx;
+  int64_t ld;
+  int T, k;
+  int chunk, n_chunks;
+};
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+constexpr int kTopkMaxChunk = 16384;
+constexpr int kTopkMaxCand = 16384;
+constexpr int kTopkMaxK = 2048;
+
+struct AttnParams {
+  const uint16_t* q;
+  int64_t q_stride;
+  const uint8_t* lat_nope;
+  const uint16_t* lat_rope;
+  const int32_t* page_table;
+  const int32_t* n_comp;
+  const int32_t* topk;     // [T][k] or nullptr (all visible entries)
+  const uint8_t* swa_nope;
+  const uint16_t* swa_rope;
+  const int32_t* swa_pos;  // ring positions [B][W] (decode) or nullptr (prefill)
+  const int32_t* q_pos;
+  const float* sink;
+  uint16_t* out;
+  float* lse;
+  float* part;             // [n_splits][T][H][D + 2] or nullptr
+  float lat_scale, swa_scale;
+  float sm_scale;          // softmax scale (natural-log units)
+  int num_pages, page_size, max_pages, ratio_m;
+  int k, W;
+  int prefill_seq;         // -1: decode (query t belongs to sequence t)
+  int swa_first_pos, swa_len;
+  int T, H;
+  int D_nope, D_rope;
+  int n_hg, n_splits, per_split;
+};
+hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
+constexpr int kAttnMaxSlots = 2048;   // key slots one workgroup handles
+constexpr int kAttnTile = 64;
+
+}  // namespace csa

@@ -1,0 +1,186 @@
+"""GPU parity of the HIP path (through the C ABI) against the FP64 oracle.
+
+Sizes: small workloads with the production head/latent shapes (128 heads,
+448 FP8 + 64 BF16 dims, 64 x 128 indexer) spanning several 64-key tiles and
+ragged tails, the tiny configuration (8 heads, 48 + 16 dims, 4 x 32 indexer),
+HCA mode, prefill, and every full-size configuration in the launch shape the
+benchmark times, checked on sampled queries.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import csa_inputs as ci
+import oracle
+from tests import parity as P
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import sparse_compressed_attention_amd as csa  # noqa: E402
+from csa_inputs.device import to_device, make_path  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(wl):
+    d = to_device(wl, "cuda")
+    path = make_path(d)
+    out, lse = path.run()
+    torch.cuda.synchronize()
+    res = dict(o=out.float().cpu().numpy().astype(np.float64), lse=lse.cpu().numpy().astype(np.float64))
+    if getattr(path, "scores", None) is not None:
+        res["scores"] = path.scores.cpu().numpy()
+        res["n_vis"] = path.n_vis.cpu().numpy()
+        res["topk"] = path.topk.cpu().numpy()
+    return res
+
+
+def check_full(wl, queries=None, exact_topk_expected=None):
+    """Run the whole path on the GPU and compare the listed queries."""
+    s = wl.spec
+    res = run_gpu(wl)
+    qs = list(range(wl.T)) if queries is None else list(queries)
+    worst = (0.0, 1.0)
+    sc_err = 0.0
+    exact = 0
+    for t in qs:
+        b = int(wl.q_seq[t])
+        nv = oracle.n_visible(int(wl.q_pos[t]), s.m, int(wl.n_comp[b]))
+        if wl.q_idx is not None:
+            assert int(res["n_vis"][t]) == nv
+            ref_scores = oracle.index_scores(wl, t)
+            sc_err = max(sc_err, P.check_scores(res["scores"][t][:nv], ref_scores) or 0.0)
+            P.check_topk_exact_on_gpu_scores(res["topk"][t], res["scores"][t][:nv], s.k)
+            exact += P.check_topk_vs_oracle(res["topk"][t], ref_scores, s.k)
+            sel = res["topk"][t]
+        else:
+            sel = None
+        o_ref, l_ref = P.reference_attention_on(wl, t, sel)
+        err, cos = P.check_attention(res["o"][t], res["lse"][t], o_ref, l_ref)
+        worst = (max(worst[0], err), min(worst[1], cos))
+    say(f"  {s.name}: {len(qs)} queries, max|err| {worst[0]:.3e}, min cos {worst[1]:.6f}, "
+        f"score err {sc_err:.2e} of row max, exact top-k sets {exact}/{len(qs)}")
+    return res
+
+
+# --------------------------------------------------------------- small shapes
+def test_tiny_config_c0():
+    say("case c0")
+    check_full(ci.make_config("c0"))
+
+
+def test_small_production_shapes_ragged():
+    say("case small ragged (3 seqs, one with fewer visible entries than k)")
+    check_full(ci.generate(ci.small_spec(shuffle_pages=True), seed=101))
+
+
+def test_small_many_sequences_non_multiple_tiles():
+    say("case small 7 seqs")
+    spec = ci.small_spec(ctx_lens=[4096, 2052, 2500, 3333 // 4 * 4, 1028, 4100, 2600], shuffle_pages=True, k=384)
+    check_full(ci.generate(spec, seed=102))
+
+
+def test_hca_mode_small():
+    say("case hca small")
+    spec = ci.small_spec(name="hca_small", ctx_lens=[20000, 9000, 41000], m=128, with_indexer=False)
+    check_full(ci.generate(spec, seed=103))
+
+
+def test_prefill_small():
+    say("case prefill small")
+    spec = ci.Spec(name="prefill_small", kind="prefill", ctx_lens=[6000], T_prefill=70)
+    check_full(ci.generate(spec, seed=104), queries=[0, 1, 17, 33, 50, 69])
+
+
+def test_ring_permutation_invariance_gpu():
+    say("case ring permutation")
+    wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1800]), seed=105)
+    a = run_gpu(wl)
+    b = run_gpu(ci.with_ring_permuted(wl, seed=7))
+    assert np.array_equal(a["topk"], b["topk"])
+    assert np.abs(a["o"] - b["o"]).max() <= 1e-2
+    for t in range(wl.T):
+        o_ref, l_ref = P.reference_attention_on(wl, t, a["topk"][t])
+        P.check_attention(b["o"][t], b["lse"][t], o_ref, l_ref)
+
+
+def test_sink_neg_inf_and_large():
+    say("case sinks")
+    wl = ci.generate(ci.small_spec(ctx_lens=[2600, 900]), seed=106)
+    wl.sink[:] = -np.inf
+    check_full(wl)
+    wl.sink[:] = 6.0
+    wl.sink[::3] = -np.inf
+    check_full(wl)
+
+
+def test_ties_go_to_lower_index():
+    """Duplicate key rows make exact score ties; the selection is still the
+    deterministic rule (lower index wins)."""
+    say("case ties")
+    wl = ci.generate(ci.small_spec(ctx_lens=[4000], k=256), seed=107)
+    s = wl.spec
+    flat = wl.k_idx.reshape(-1, s.D_I)
+    rows = oracle.entry_rows(wl.page_table[0], s.page_size, np.arange(int(wl.n_comp[0])))
+    # every group of 8 consecutive entries shares one key
+    for c in range(0, len(rows), 8):
+        flat[rows[c:c + 8]] = flat[rows[c]]
+    res = check_full(wl)
+    sc = res["scores"][0][:int(res["n_vis"][0])]
+    assert len(np.unique(sc)) < len(sc) // 4
+
+
+def test_poisoned_future_blocks_never_selected():
+    say("case causality poison")
+    spec = ci.small_spec(ctx_lens=[4000, 3000], q_pos=[2501, 1999])
+    wl = ci.generate(spec, seed=108)
+    s = wl.spec
+    for t in range(wl.T):
+        b = int(wl.q_seq[t])
+        nv = oracle.n_visible(int(wl.q_pos[t]), s.m, int(wl.n_comp[b]))
+        rows = oracle.entry_rows(wl.page_table[b], s.page_size, np.arange(nv, int(wl.n_comp[b])))
+        wl.k_idx.reshape(-1, s.D_I)[rows] = wl.q_idx[t][0]
+    res = check_full(wl)
+    for t in range(wl.T):
+        nv = int(res["n_vis"][t])
+        sel = res["topk"][t]
+        assert np.all(sel[sel >= 0] < nv)
+
+
+def test_empty_window_and_no_visible_entries():
+    """A query at position 2 sees no compressed entry (own block) and only the
+    3 window tokens that exist."""
+    say("case empty")
+    spec = ci.small_spec(ctx_lens=[3, 700], k=64)
+    check_full(ci.generate(spec, seed=109))
+
+
+# --------------------------------------------------------------- full sizes
+@pytest.mark.parametrize("name,queries", [
+    ("c1", [0]),
+    ("c2", [0, 17, 40, 63]),
+    ("c3_csa", [1, 3]),
+    ("c3_hca", [0, 2]),
+    ("c4", [0, 511, 1024, 2047]),
+])
+def test_full_size_configs_sampled(name, queries):
+    say(f"case full {name}")
+    check_full(ci.make_config(name), queries=queries)
+
+
+def test_deterministic_repeat():
+    say("case determinism")
+    wl = ci.generate(ci.small_spec(), seed=110)
+    a = run_gpu(wl)
+    b = run_gpu(wl)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
