@@ -54,7 +54,22 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle's CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="device copies of the inputs (0 = enough for 1 GB)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times), to calibrate HBM byte counters")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counter
+    readings give the factor between those counters and bytes moved."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}), flush=True)
 
 
 # --------------------------------------------------------------- accounting
@@ -191,6 +206,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     csa.load_library()
     torch.cuda.set_device(0)
     dev = "cuda:0"

@@ -19,21 +19,29 @@
 //  * wave (ht, kh): heads [16 ht, 16 ht + 16) of the group; within every
 //    64-key tile it takes keys [32 kh, 32 kh + 32).  The two kh waves of a head
 //    tile merge their softmax states through LDS at the end;
-//  * the tile is gathered from HBM (top-k index -> page table -> row) into
-//    registers and then LDS, double-buffered, in the cache's own FP8/BF16
-//    bytes;
+//  * gather: key descriptors (top-k index -> page table -> row, or window slot
+//    -> row) are resolved once into LDS; each 64-key tile is copied from HBM
+//    straight into LDS with global_load_lds_dwordx4 (no register staging),
+//    three tiles in flight (ring of 3 buffers, prefetch distance 2).  The
+//    tile is stored as "planes": plane c holds the c-th 16-byte chunk of all
+//    64 rows, so one DMA instruction writes one whole plane and every lane
+//    keeps one row (key) for all of its DMAs.  Rows 16..31 and 48..63 are
+//    XOR-swizzled by 4 slots so that the transpose reads below never hit the
+//    same LDS banks.  The cache's FP8/BF16 bytes go to the MFMA unchanged;
 //  * QK: S^T (keys x heads) = X . Q^T on v_mfma 16x16x128 FP8, with q split
 //    into two E4M3 terms hi + lo sharing a power-of-two per-head scale (the K
 //    dimension is [hi | lo], X read once and used for both), plus the rope
-//    dims on v_mfma 16x16x32 BF16.  The key scale and the softmax scale are
-//    applied per lane in FP32;
+//    dims on v_mfma 16x16x32 BF16; the two 16-key subtiles are interleaved
+//    and the next X operands are read from LDS before the current MFMAs;
 //  * online softmax in FP32, exp2 domain; each lane owns one head, so the
-//    rescale of O needs no cross-lane traffic; the sink starts the running
-//    max and denominator (zero value);
+//    rescale of O needs no cross-lane traffic.  The running max is raised
+//    lazily: only when a tile's max exceeds it by more than 2^tau (tau = 4),
+//    so probabilities stay <= 2^tau and the O rescale runs on few tiles.  The
+//    sink starts the running max and denominator (zero value);
 //  * PV: O^T (dims x heads) += X^T . P^T: X^T is read from the same LDS tile
 //    with ds_read_b64_tr_b8 (nope, FP8; P as two E4M3 terms hi + lo after a
-//    2^8 scale) and ds_read_b64_tr_b16 (rope, BF16, P in BF16); P never leaves
-//    registers.
+//    2^(8 - tau) scale) and ds_read_b64_tr_b16 (rope, BF16, P in BF16); bytes
+//    of masked keys are cleared in registers; P never leaves registers.
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -42,12 +50,11 @@ namespace csa {
 namespace {
 
 constexpr int kSwaFlag = 1 << 30;
+constexpr int kNBuf = 3;
+constexpr int kPlane = kAttnTile * 16;   // bytes per plane (64 rows x 16 B)
 
 template <int DN, int DR>
 struct Cfg {
-  static constexpr int NP = ((DN / 16) % 2 == 0) ? DN + 16 : DN;          // LDS pitch, nope
-  static constexpr int RB = 2 * DR;                                          // rope bytes
-  static constexpr int RP = ((RB / 16) % 2 == 0) ? RB + 16 : RB;          // LDS pitch, rope
   static constexpr int NFB = DN / 128;                                       // full 128-dim blocks
   static constexpr int REM = DN % 128;                                       // combined hi|lo block
   static constexpr int NR = (DR + 31) / 32;                                  // rope k-steps
@@ -55,41 +62,61 @@ struct Cfg {
   static constexpr int NDR = DR / 16;                                        // PV rope dim tiles
   static constexpr int NDT = ND + NDR;
   static constexpr int HALF = NDT / 2;
-  static constexpr int CHN = DN / 16;                                        // 16-byte chunks / key
-  static constexpr int CHR = RB / 16;
+  static constexpr int CHN = DN / 16;                                        // nope planes
+  static constexpr int CHR = 2 * DR / 16;                                    // rope planes
   static constexpr int CH = CHN + CHR;
-  static constexpr int CPT = (CH + 3) / 4;                                   // chunks per thread
-  static constexpr int TILE_BYTES = kAttnTile * (NP + RP);
+  static constexpr int PPW = (CH + 3) / 4;                                   // planes per wave (max)
+  static constexpr int PMIN = CH / 4;                                        // planes per wave (min)
+  static constexpr int TILE_BYTES = CH * kPlane;
   static_assert(DN % 16 == 0 && DR % 16 == 0, "dims must be multiples of 16");
   static_assert(REM <= 64, "remainder block must fit one combined hi|lo MFMA");
   static_assert(NDT % 2 == 0, "dim tiles split evenly between the two key halves");
+  static_assert(PMIN >= 1, "every wave issues at least one plane per tile");
 };
 
 // key (0..31) of this wave's half-tile held by byte e (0..7) of a lane in
 // 16-lane group g, as produced by the QK output layout of two 16-key subtiles.
 __device__ __forceinline__ int kappa(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+// LDS slot of key k inside a plane (an involution).
+__device__ __forceinline__ int slot_of(int k) { return k ^ (((k >> 4) & 1) << 2); }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
 
 template <int DN, int DR>
 __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
   using C = Cfg<DN, DR>;
   constexpr int D = DN + DR;
 
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf][C::TILE_BYTES];
   __shared__ int32_t desc[kAttnMaxSlots];
 
-  // ---- which (query, head group, split): queries are spread over the 8
-  // XCDs round-robin and all workgroups of one query share an XCD (and its L2).
+  // ---- which (query, head group, split).  Workgroups go to the 8 XCDs
+  // round-robin by id.  With 8 or more queries, queries are spread over the
+  // XCDs and all workgroups of one query share an XCD (and its L2, which then
+  // serves the head groups' repeated reads of the same rows); with fewer,
+  // a query's workgroups are spread over all XCDs instead.
   const int nb = p.n_hg * p.n_splits;
   const int bid = blockIdx.x;
-  const int local = bid >> 3;
-  const int t = (local / nb) * 8 + (bid & 7);
+  int t, jb;
+  if (p.T >= 8) {
+    const int local = bid >> 3;
+    t = (local / nb) * 8 + (bid & 7);
+    jb = local % nb;
+  } else {
+    t = bid / nb;
+    jb = bid - t * nb;
+  }
   if (t >= p.T) return;
-  const int jb = local % nb;
   const int hg = jb / p.n_splits;
   const int split = jb - hg * p.n_splits;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r = lane & 15;
   const int ht = wave & 1;
@@ -109,40 +136,13 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
   const int kv1 = min(n_slots, kv0 + p.per_split);
   const int nkeys = max(0, kv1 - kv0);
 
-  // ---- key descriptors of this workgroup's slots: row | source flag, -1 = skip
-  const int32_t* pt = p.page_table + (size_t)seq * p.max_pages;
-  for (int s = threadIdx.x; s < nkeys; s += 256) {
-    const int slot = kv0 + s;
-    int d = -1;
-    if (slot < n_sel) {
-      const int idx = p.topk ? p.topk[(size_t)t * p.k + slot] : slot;
-      if (idx >= 0 && idx < nc && idx / p.page_size < p.max_pages) {
-        const int page = pt[idx / p.page_size];
-        if (page >= 0 && page < p.num_pages) d = page * p.page_size + idx % p.page_size;
-      }
-    } else {
-      const int j = slot - n_sel;
-      if (!prefill) {
-        const int pp = p.swa_pos[(size_t)seq * p.W + j];
-        if (pp >= 0 && pp <= pos && pp > pos - p.W) d = (seq * p.W + j) | kSwaFlag;
-      } else {
-        const int pp = pos - p.W + 1 + j;
-        if (pp >= 0 && pp >= p.swa_first_pos && pp - p.swa_first_pos < p.swa_len)
-          d = (pp - p.swa_first_pos) | kSwaFlag;
-      }
-    }
-    desc[s] = d;
-  }
-
-  // ---- query operands (registers for the whole kernel)
-  v8i qhi[C::NFB > 0 ? C::NFB : 1], qlo[C::NFB > 0 ? C::NFB : 1], qcomb;
-  v8bf qr[C::NR];
-  float cq = 0.0f;
-  const float cr = p.sm_scale * kLog2e;
+  // ---- query rows: loads issued first (packed BF16, 64 VGPRs) so their
+  // latency overlaps the descriptor round trips; converted after the first
+  // tile DMAs are issued
+  v4i qraw[C::NFB + 1][4];
+  v4i qrope[C::NR];
   {
     const uint16_t* qrow = p.q + (size_t)t * p.q_stride + (size_t)h * D;
-    float v[C::NFB + 1][32];
-    float amax = 0.0f;
 #pragma unroll
     for (int b = 0; b <= C::NFB; ++b) {
       const bool comb = (b == C::NFB);
@@ -152,15 +152,128 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
         const int dd = d0 + 8 * c;
         v4i raw = (v4i){0, 0, 0, 0};
         if (head_ok && (!comb || C::REM > 0) && dd < DN) raw = ld16(qrow + dd);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w = (uint32_t)raw[e >> 1];
-          const float f = bf16_bits_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
-          v[b][8 * c + e] = f;
-          amax = fmaxf(amax, fabsf(f));
-        }
+        qraw[b][c] = raw;
       }
     }
+#pragma unroll
+    for (int rr = 0; rr < C::NR; ++rr) {
+      const int dd = 32 * rr + 8 * g;
+      v4i raw = (v4i){0, 0, 0, 0};
+      if (head_ok && dd < DR) raw = ld16(qrow + DN + dd);
+      qrope[rr] = raw;
+    }
+  }
+  const float sink_raw = head_ok ? p.sink[h] : 0.0f;
+
+  // ---- key descriptors of this workgroup's slots: row | source flag, -1 =
+  // skip.  All first-level loads (top-k index or ring position) are issued
+  // together, then all page-table loads: two round trips in total.
+  const int32_t* pt = p.page_table + (size_t)seq * p.max_pages;
+  constexpr int kSPT = kAttnMaxSlots / 256;   // slots per thread
+  int v1[kSPT];
+#pragma unroll
+  for (int j = 0; j < kSPT; ++j) {
+    const int s = threadIdx.x + 256 * j;
+    const int slot = kv0 + s;
+    int v = -1;
+    if (s < nkeys) {
+      if (slot < n_sel) {
+        v = p.topk ? p.topk[(size_t)t * p.k + slot] : slot;
+      } else if (!prefill) {
+        v = p.swa_pos[(size_t)seq * p.W + (slot - n_sel)];
+      }
+    }
+    v1[j] = v;
+  }
+  int v2[kSPT];
+#pragma unroll
+  for (int j = 0; j < kSPT; ++j) {
+    const int s = threadIdx.x + 256 * j;
+    const int slot = kv0 + s;
+    const int idx = v1[j];
+    int page = -1;
+    if (s < nkeys && slot < n_sel && idx >= 0 && idx < nc && idx / p.page_size < p.max_pages)
+      page = pt[idx / p.page_size];
+    v2[j] = page;
+  }
+#pragma unroll
+  for (int j = 0; j < kSPT; ++j) {
+    const int s = threadIdx.x + 256 * j;
+    if (s >= nkeys) continue;
+    const int slot = kv0 + s;
+    int d = -1;
+    if (slot < n_sel) {
+      const int idx = v1[j], page = v2[j];
+      if (page >= 0 && page < p.num_pages) d = page * p.page_size + idx % p.page_size;
+    } else {
+      const int jw = slot - n_sel;
+      if (!prefill) {
+        const int pp = v1[j];
+        if (pp >= 0 && pp <= pos && pp > pos - p.W) d = (seq * p.W + jw) | kSwaFlag;
+      } else {
+        const int pp = pos - p.W + 1 + jw;
+        if (pp >= 0 && pp >= p.swa_first_pos && pp - p.swa_first_pos < p.swa_len)
+          d = (pp - p.swa_first_pos) | kSwaFlag;
+      }
+    }
+    desc[s] = d;
+  }
+
+  __syncthreads();   // descriptors visible
+
+  // ---- tile DMA: lane -> the key whose plane slot is `lane`, planes
+  // c = wave + 4 i.  Masked keys copy a dummy row (row 0) so that every wave
+  // issues the same number of DMAs per tile; their bytes are never used.
+  const int dkey = slot_of(lane);
+  auto issue_tile = [&](int tile, int buf) {
+    const int s = tile * kAttnTile + dkey;
+    const int d = s < nkeys ? desc[s] : -1;
+    const uint8_t* nsrc = p.lat_nope;
+    const uint8_t* rsrc = reinterpret_cast<const uint8_t*>(p.lat_rope);
+    if (d >= 0) {
+      const size_t row = (size_t)(d & ~kSwaFlag);
+      if (d & kSwaFlag) {
+        nsrc = p.swa_nope + row * DN;
+        rsrc = reinterpret_cast<const uint8_t*>(p.swa_rope + row * DR);
+      } else {
+        nsrc = p.lat_nope + row * DN;
+        rsrc = reinterpret_cast<const uint8_t*>(p.lat_rope + row * DR);
+      }
+    }
+    uint8_t* base = xs[buf];
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) {
+      const int c = wave + 4 * i;
+      if (c < C::CH) {
+        const uint8_t* src = (c < C::CHN) ? nsrc + 16 * c : rsrc + 16 * (c - C::CHN);
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void CSA_LDS*)(base + c * kPlane), 16, 0, 0);
+      }
+    }
+  };
+
+  const int n_tiles = (nkeys + kAttnTile - 1) / kAttnTile;
+  if (n_tiles > 0) issue_tile(0, 0);
+  if (n_tiles > 1) issue_tile(1, 1);
+
+  // ---- query operands: q split into two E4M3 terms hi + lo with a shared
+  // power-of-two per-head scale (registers for the whole kernel)
+  v8i qhi[C::NFB > 0 ? C::NFB : 1], qlo[C::NFB > 0 ? C::NFB : 1], qcomb;
+  v8bf qr[C::NR];
+  float cq = 0.0f;
+  const float cr = p.sm_log2;
+  {
+    auto qval = [&](int b, int c, int e) -> float {
+      const uint32_t w = (uint32_t)qraw[b][c][e >> 1];
+      return bf16_bits_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+    };
+    float amax = 0.0f;
+#pragma unroll
+    for (int b = 0; b <= C::NFB; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(qval(b, c, e)));
     amax = max_over_groups(amax);
     const float s = e4m3_pow2_scale(amax);
     const float inv = 1.0f / s;
@@ -172,7 +285,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
       for (int w4 = 0; w4 < 8; ++w4) {
         float x[4], res[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = v[b][4 * w4 + e] * inv;
+        for (int e = 0; e < 4; ++e) x[e] = qval(b, w4 >> 1, 4 * (w4 & 1) + e) * inv;
         const int hw = pack4_fp8(x[0], x[1], x[2], x[3]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) res[e] = x[e] - fp8_to_f32(hw, e);
@@ -187,12 +300,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < C::NR; ++rr) {
-      const int dd = 32 * rr + 8 * g;
-      v4i raw = (v4i){0, 0, 0, 0};
-      if (head_ok && dd < DR) raw = ld16(qrow + DN + dd);
-      qr[rr] = __builtin_bit_cast(v8bf, raw);
-    }
+    for (int rr = 0; rr < C::NR; ++rr) qr[rr] = __builtin_bit_cast(v8bf, qrope[rr]);
   }
   if (C::NFB == 0) {
     qhi[0] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
@@ -201,199 +309,208 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
 
   // ---- softmax state (exp2 domain); only one wave per head carries the sink
   const bool sink_here = split == 0 && kh == 0 && head_ok;
-  const float sink2 = head_ok ? p.sink[h] * kLog2e : -__builtin_inff();
+  const float sink2 = head_ok ? sink_raw * kLog2e : -__builtin_inff();
   float m_run = sink_here ? sink2 : -__builtin_inff();
   float l_run = (sink_here && g == 0 && sink2 > -__builtin_inff()) ? 1.0f : 0.0f;
   v4f O[C::NDT];
 #pragma unroll
   for (int i = 0; i < C::NDT; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  const float smax = fmaxf(p.lat_scale, p.swa_scale);
-  const float ratio_lat = p.lat_scale / smax * 256.0f;
-  const float ratio_swa = p.swa_scale / smax * 256.0f;
 
-  __syncthreads();   // descriptors visible
+  const int sl_q0 = slot_of(32 * kh + r);          // QK rows of subtile 0 / 1
+  const int sl_q1 = slot_of(32 * kh + 16 + r);
+  int buf = 0;
+  for (int it = 0; it < n_tiles; ++it, buf = (buf + 1 == kNBuf) ? 0 : buf + 1) {
+    // tile `it` landed in LDS (this wave's DMAs), then everyone's (barrier);
+    // the barrier also retires every wave's reads of the buffer reused next
+    if (it + 1 < n_tiles) wait_vmcnt<C::PMIN>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (it + 2 < n_tiles) issue_tile(it + 2, buf == 0 ? 2 : buf - 1);
+    if (!tile_ok) continue;
+    const uint8_t* xb = xs[buf];
 
-  // ---- tile staging: thread -> key (tid / 4), chunks (tid % 4) + 4 j
-  const int skey = threadIdx.x >> 2;
-  const int spart = threadIdx.x & 3;
-  v4i stage[C::CPT];
-  auto load_tile = [&](int tile) {
-    const int s = tile * kAttnTile + skey;
-    const int d = s < nkeys ? desc[s] : -1;
-    const uint8_t* nsrc = nullptr;
-    const uint8_t* rsrc = nullptr;
-    if (d >= 0) {
-      const size_t row = (size_t)(d & ~kSwaFlag);
-      if (d & kSwaFlag) {
-        nsrc = p.swa_nope + row * DN;
-        rsrc = reinterpret_cast<const uint8_t*>(p.swa_rope + row * DR);
+    // -- QK for the wave's two 16-key subtiles, interleaved
+    auto xread = [&](int sl, int c0) -> v8i {
+      const v4i lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + 16 * sl);
+      const v4i hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + 16 * sl);
+      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto xcomb = [&](int sl) -> v8i {
+      const int c0 = 8 * C::NFB + 2 * (g & 1);
+      v8i x = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+      if (32 * (g & 1) < C::REM) {
+        const v4i lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + 16 * sl);
+        v4i hi = (v4i){0, 0, 0, 0};
+        if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + 16 * sl);
+        x = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      return x;
+    };
+    v4f a0 = (v4f){0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    v8i x0, x1;
+    if (C::NFB > 0) {
+      x0 = xread(sl_q0, 2 * g);
+      x1 = xread(sl_q1, 2 * g);
+    } else {
+      x0 = xcomb(sl_q0);
+      x1 = xcomb(sl_q1);
+    }
+#pragma unroll
+    for (int b = 0; b < C::NFB; ++b) {
+      v8i n0, n1;
+      if (b + 1 < C::NFB) {
+        n0 = xread(sl_q0, 8 * (b + 1) + 2 * g);
+        n1 = xread(sl_q1, 8 * (b + 1) + 2 * g);
       } else {
-        nsrc = p.lat_nope + row * DN;
-        rsrc = reinterpret_cast<const uint8_t*>(p.lat_rope + row * DR);
+        n0 = xcomb(sl_q0);
+        n1 = xcomb(sl_q1);
       }
+      a0 = mfma_f8_128(x0, qhi[b], a0);
+      a1 = mfma_f8_128(x1, qhi[b], a1);
+      a0 = mfma_f8_128(x0, qlo[b], a0);
+      a1 = mfma_f8_128(x1, qlo[b], a1);
+      x0 = n0;
+      x1 = n1;
     }
-#pragma unroll
-    for (int j = 0; j < C::CPT; ++j) {
-      const int c = spart + 4 * j;
-      v4i x = (v4i){0, 0, 0, 0};
-      if (d >= 0 && c < C::CH) x = (c < C::CHN) ? ld16(nsrc + 16 * c) : ld16(rsrc + 16 * (c - C::CHN));
-      stage[j] = x;
+    if (C::REM > 0) {
+      a0 = mfma_f8_128(x0, qcomb, a0);
+      a1 = mfma_f8_128(x1, qcomb, a1);
     }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* base = xs[buf];
+    v4f r0 = (v4f){0.f, 0.f, 0.f, 0.f}, r1 = r0;
 #pragma unroll
-    for (int j = 0; j < C::CPT; ++j) {
-      const int c = spart + 4 * j;
-      if (c < C::CH) {
-        uint8_t* dst = (c < C::CHN) ? base + skey * C::NP + 16 * c
-                                    : base + kAttnTile * C::NP + skey * C::RP + 16 * (c - C::CHN);
-        *reinterpret_cast<v4i*>(dst) = stage[j];
+    for (int rr = 0; rr < C::NR; ++rr) {
+      const int c = C::CHN + 4 * rr + g;
+      v4i y0 = (v4i){0, 0, 0, 0}, y1 = y0;
+      if (32 * rr + 8 * g < DR) {
+        y0 = *reinterpret_cast<const v4i*>(xb + c * kPlane + 16 * sl_q0);
+        y1 = *reinterpret_cast<const v4i*>(xb + c * kPlane + 16 * sl_q1);
       }
+      r0 = mfma_bf16_32(__builtin_bit_cast(v8bf, y0), qr[rr], r0);
+      r1 = mfma_bf16_32(__builtin_bit_cast(v8bf, y1), qr[rr], r1);
     }
-  };
 
-  const int n_tiles = (nkeys + kAttnTile - 1) / kAttnTile;
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_tiles) load_tile(it + 1);
-    if (tile_ok) {
-      const uint8_t* xn = xs[buf];
-      const uint8_t* xr = xs[buf] + kAttnTile * C::NP;
-      // -- QK for the wave's two 16-key subtiles
-      v4f an[2], ar[2];
+    // -- online softmax (lane: head h, keys kappa(g, e) of this half-tile)
+    float sv[8], kq[8];
+    uint32_t m8lo = 0, m8hi = 0;   // byte masks of the valid keys (PV operands)
+    float tmax = -__builtin_inff();
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int kr = 32 * kh + 16 * st + r;
-        v4f a = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < C::NFB; ++b) {
-          const uint8_t* src = xn + kr * C::NP + 128 * b + 32 * g;
-          const v4i x0 = *reinterpret_cast<const v4i*>(src);
-          const v4i x1 = *reinterpret_cast<const v4i*>(src + 16);
-          const v8i xa = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          a = mfma_f8_128(xa, qhi[b], a);
-          a = mfma_f8_128(xa, qlo[b], a);
-        }
-        if (C::REM > 0) {
-          const int off = 32 * (g & 1);
-          const uint8_t* src = xn + kr * C::NP + 128 * C::NFB + off;
-          v8i xa = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-          if (off < C::REM) {
-            const v4i x0 = *reinterpret_cast<const v4i*>(src);
-            v4i x1 = (v4i){0, 0, 0, 0};
-            if (off + 16 < C::REM) x1 = *reinterpret_cast<const v4i*>(src + 16);
-            xa = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          }
-          a = mfma_f8_128(xa, qcomb, a);
-        }
-        an[st] = a;
-        v4f b2 = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int rr = 0; rr < C::NR; ++rr) {
-          const int dd = 32 * rr + 8 * g;
-          v4i x = (v4i){0, 0, 0, 0};
-          if (dd < DR) x = *reinterpret_cast<const v4i*>(xr + kr * C::RP + 2 * dd);
-          b2 = mfma_bf16_32(__builtin_bit_cast(v8bf, x), qr[rr], b2);
-        }
-        ar[st] = b2;
+    for (int e = 0; e < 8; ++e) {
+      const int st = e >> 2, i = e & 3;
+      const int s = it * kAttnTile + 32 * kh + 16 * st + 4 * g + i;   // = key kappa(g, e)
+      const int d = s < nkeys ? desc[s] : -1;
+      const bool swa = (d & kSwaFlag) != 0;
+      const float an = st ? a1[i] : a0[i];
+      const float ar = st ? r1[i] : r0[i];
+      const float x = cq * (swa ? p.swa_scale : p.lat_scale) * an + cr * ar;
+      kq[e] = swa ? p.pscale_swa : p.pscale_lat;
+      sv[e] = (d >= 0 && head_ok) ? x : -__builtin_inff();
+      tmax = fmaxf(tmax, sv[e]);
+      if (d >= 0) {
+        if (e < 4) m8lo |= 0xffu << (8 * e);
+        else m8hi |= 0xffu << (8 * (e - 4));
       }
-      // -- online softmax (lane: head h, keys kappa(g, e))
-      float sv[8], kq[8];
-      float tmax = -__builtin_inff();
+    }
+    tmax = max_over_groups(tmax);
+    const bool grow = tmax > m_run + (float)kAttnTau;
+    if (__ballot(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int st = e >> 2, i = e & 3;
-        const int s = it * kAttnTile + 32 * kh + 16 * st + 4 * g + i;
-        const int d = s < nkeys ? desc[s] : -1;
-        const bool swa = (d & kSwaFlag) != 0;
-        const float ks = swa ? p.swa_scale : p.lat_scale;
-        kq[e] = swa ? ratio_swa : ratio_lat;
-        const float x = cq * ks * an[st][i] + cr * ar[st][i];
-        sv[e] = (d >= 0 && head_ok) ? x : -__builtin_inff();
-        tmax = fmaxf(tmax, sv[e]);
-      }
-      tmax = max_over_groups(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float msub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-      const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - msub);
-      float pr[8];
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pr[e] = (sv[e] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sv[e] - msub);
-        psum += pr[e];
-      }
-      l_run = l_run * alpha + psum;
+      for (int i = 0; i < C::NDT; ++i) O[i] *= alpha;
       m_run = m_new;
-      if (__ballot(alpha != 1.0f)) {
+    }
+    const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+    float pr[8];
+    float psum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < C::NDT; ++i) O[i] *= alpha;
-      }
-      // -- P operands for nope: two E4M3 terms hi + lo of p x 2^8 x key-scale
-      //    ratio (lo = the rounding residual of hi); BF16 for rope
-      float px[8], pres[8];
+    for (int e = 0; e < 8; ++e) {
+      pr[e] = (sv[e] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sv[e] - msub);
+      psum += pr[e];
+    }
+    l_run += psum;
+    // -- P operands for nope: two E4M3 terms hi + lo of p x key-scale ratio x
+    //    2^(8 - tau) (lo = the rounding residual of hi); BF16 for rope
+    float px[8], pres[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) px[e] = pr[e] * kq[e];
-      const int w0 = pack4_fp8(px[0], px[1], px[2], px[3]);
-      const int w1 = pack4_fp8(px[4], px[5], px[6], px[7]);
+    for (int e = 0; e < 8; ++e) px[e] = pr[e] * kq[e];
+    const int w0 = pack4_fp8(px[0], px[1], px[2], px[3]);
+    const int w1 = pack4_fp8(px[4], px[5], px[6], px[7]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pres[e] = px[e] - fp8_to_f32(w0, e);
-        pres[4 + e] = px[4 + e] - fp8_to_f32(w1, e);
-      }
-      const int w0l = pack4_fp8(pres[0], pres[1], pres[2], pres[3]);
-      const int w1l = pack4_fp8(pres[4], pres[5], pres[6], pres[7]);
-      const long p8 = (long)(uint32_t)w0 | ((long)(uint32_t)w1 << 32);
-      const long p8l = (long)(uint32_t)w0l | ((long)(uint32_t)w1l << 32);
-      v4i pbw;
+    for (int e = 0; e < 4; ++e) {
+      pres[e] = px[e] - fp8_to_f32(w0, e);
+      pres[4 + e] = px[4 + e] - fp8_to_f32(w1, e);
+    }
+    const int w0l = pack4_fp8(pres[0], pres[1], pres[2], pres[3]);
+    const int w1l = pack4_fp8(pres[4], pres[5], pres[6], pres[7]);
+    const long p8 = (long)(uint32_t)w0 | ((long)(uint32_t)w1 << 32);
+    const long p8l = (long)(uint32_t)w0l | ((long)(uint32_t)w1l << 32);
+    v4i pbw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pbw[e] = (int)((uint32_t)f32_to_bf16_bits(pr[2 * e]) | ((uint32_t)f32_to_bf16_bits(pr[2 * e + 1]) << 16));
-      const v8bf pbf = __builtin_bit_cast(v8bf, pbw);
-      // -- PV: O^T[dims x heads] += X^T[dims x keys] P^T[keys x heads]
-      {
-        const int krow = 32 * kh + kappa(g, r >> 1);
-        const uint8_t* a8 = xn + krow * C::NP + 8 * (r & 1);
+    for (int e = 0; e < 4; ++e)
+      pbw[e] = (int)((uint32_t)f32_to_bf16_bits(pr[2 * e]) | ((uint32_t)f32_to_bf16_bits(pr[2 * e + 1]) << 16));
+    const v8bf pbf = __builtin_bit_cast(v8bf, pbw);
+
+    // -- PV: O^T[dims x heads] += X^T[dims x keys] P^T[keys x heads].  The
+    //    X^T bytes of masked keys are cleared (their LDS rows are a dummy copy)
+    {
+      const int krow = 32 * kh + kappa(g, r >> 1);
+      const uint8_t* a8 = xb + 16 * slot_of(krow) + 8 * (r & 1);
+      // transpose reads in batches of PVB issued ahead of their MFMAs
+      constexpr int PVB = 7;
+      static_assert(C::ND % PVB == 0 || C::ND < PVB, "PV batch");
+      constexpr int NB = C::ND < PVB ? 1 : C::ND / PVB;
+      constexpr int BS = C::ND < PVB ? C::ND : PVB;
+      v2i abuf[2][BS];
 #pragma unroll
-        for (int dt = 0; dt < C::ND; ++dt) {
-          const v2i a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(a8 + 16 * dt));
-          const long al = (long)(uint32_t)a[0] | ((long)(uint32_t)a[1] << 32);
+      for (int j = 0; j < BS; ++j)
+        abuf[0][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(a8 + j * kPlane));
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt) {
+        if (bt + 1 < NB) {
+#pragma unroll
+          for (int j = 0; j < BS; ++j)
+            abuf[(bt + 1) & 1][j] =
+                __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(a8 + ((bt + 1) * BS + j) * kPlane));
+        }
+#pragma unroll
+        for (int j = 0; j < BS; ++j) {
+          const int dt = bt * BS + j;
+          const v2i a = abuf[bt & 1][j];
+          const long al = (long)((uint32_t)a[0] & m8lo) | ((long)((uint32_t)a[1] & m8hi) << 32);
           O[dt] = mfma_f8_32(al, p8, O[dt]);
           O[dt] = mfma_f8_32(al, p8l, O[dt]);
         }
-        const int krow0 = 32 * kh + kappa(g, r >> 2);
-        const int krow1 = 32 * kh + kappa(g, 4 + (r >> 2));
-        const uint8_t* b0 = xr + krow0 * C::RP + 8 * (r & 3);
-        const uint8_t* b1 = xr + krow1 * C::RP + 8 * (r & 3);
+      }
+      // rope, 16-bit elements: element e of read 0 / read 1 is key kappa(g, e) / kappa(g, 4 + e)
+      const uint32_t mr0 = ((m8lo & 0xffu) ? 0xffffu : 0u) | ((m8lo & 0xff00u) ? 0xffff0000u : 0u);
+      const uint32_t mr1 = ((m8lo & 0xff0000u) ? 0xffffu : 0u) | ((m8lo & 0xff000000u) ? 0xffff0000u : 0u);
+      const uint32_t mr2 = ((m8hi & 0xffu) ? 0xffffu : 0u) | ((m8hi & 0xff00u) ? 0xffff0000u : 0u);
+      const uint32_t mr3 = ((m8hi & 0xff0000u) ? 0xffffu : 0u) | ((m8hi & 0xff000000u) ? 0xffff0000u : 0u);
+      const int krow0 = 32 * kh + kappa(g, r >> 2);
+      const int krow1 = 32 * kh + kappa(g, 4 + (r >> 2));
+      const int cpl = C::CHN + ((r >> 1) & 1);
+      const uint8_t* b0 = xb + cpl * kPlane + 16 * slot_of(krow0) + 8 * (r & 1);
+      const uint8_t* b1 = xb + cpl * kPlane + 16 * slot_of(krow1) + 8 * (r & 1);
 #pragma unroll
-        for (int dt = 0; dt < C::NDR; ++dt) {
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(b0 + 32 * dt));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(b1 + 32 * dt));
-          v4i packed;
-          packed[0] = (int)((uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16));
-          packed[1] = (int)((uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16));
-          packed[2] = (int)((uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16));
-          packed[3] = (int)((uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
-          O[C::ND + dt] = mfma_bf16_32(__builtin_bit_cast(v8bf, packed), pbf, O[C::ND + dt]);
-        }
+      for (int dt = 0; dt < C::NDR; ++dt) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(b0 + 2 * dt * kPlane));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(b1 + 2 * dt * kPlane));
+        v4i packed;
+        packed[0] = (int)(((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16)) & mr0);
+        packed[1] = (int)(((uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16)) & mr1);
+        packed[2] = (int)(((uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16)) & mr2);
+        packed[3] = (int)(((uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)) & mr3);
+        O[C::ND + dt] = mfma_bf16_32(__builtin_bit_cast(v8bf, packed), pbf, O[C::ND + dt]);
       }
     }
-    if (it + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
   }
+  __syncthreads();   // every wave is done with the tile buffers
 
   // ---- merge the two key halves (kh) of each head tile through LDS
   const float l_tot = sum_over_groups(l_run);
   float* ex = reinterpret_cast<float*>(&xs[0][0]);                   // [4][HALF][64][4]
-  float* st = ex + 4 * C::HALF * 64 * 4;                               // [4][64][2]
+  float* stt = ex + 4 * C::HALF * 64 * 4;                              // [4][64][2]
   if (kh == 0) {
 #pragma unroll
     for (int j = 0; j < C::HALF; ++j)
@@ -403,26 +520,25 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
     for (int j = 0; j < C::HALF; ++j)
       *reinterpret_cast<v4f*>(ex + ((wave * C::HALF + j) * 64 + lane) * 4) = O[j];
   }
-  st[(wave * 64 + lane) * 2 + 0] = m_run;
-  st[(wave * 64 + lane) * 2 + 1] = l_tot;
+  stt[(wave * 64 + lane) * 2 + 0] = m_run;
+  stt[(wave * 64 + lane) * 2 + 1] = l_tot;
   __syncthreads();
   if (!tile_ok) return;
   const int partner = wave ^ 2;
-  const float pm = st[(partner * 64 + lane) * 2 + 0];
-  const float pl = st[(partner * 64 + lane) * 2 + 1];
+  const float pm = stt[(partner * 64 + lane) * 2 + 0];
+  const float pl = stt[(partner * 64 + lane) * 2 + 1];
   const float M = fmaxf(m_run, pm);
   const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
   const float a_self = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - Ms);
   const float a_oth = (pm == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(pm - Ms);
   const float L = l_tot * a_self + pl * a_oth;
-  const float nope_unit = smax * (1.0f / 256.0f);
   const bool final_out = p.n_splits == 1;
   const float invL = (final_out && L > 0.0f) ? 1.0f / L : 0.0f;
 
   auto finish = [&](int dt, const v4f& own) {
     const v4f oth = *reinterpret_cast<const v4f*>(ex + ((partner * C::HALF + (dt - kh * C::HALF)) * 64 + lane) * 4);
     const bool nope = dt < C::ND;
-    const float unit = nope ? nope_unit : 1.0f;
+    const float unit = nope ? p.nope_unit : 1.0f;
     const int dim = nope ? 16 * dt + 4 * g : DN + 16 * (dt - C::ND) + 4 * g;
     v4f v;
 #pragma unroll
@@ -497,7 +613,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 template <int DN, int DR>
 hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
   const int nb = p.n_hg * p.n_splits;
-  const int blocks = ((p.T + 7) / 8) * 8 * nb;
+  const int blocks = (p.T >= 8 ? ((p.T + 7) / 8) * 8 : p.T) * nb;
   hipLaunchKernelGGL((attn_kernel<DN, DR>), dim3(blocks), dim3(256), 0, stream, p);
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;

@@ -34,7 +34,7 @@ TopkPlan plan_topk(int32_t T, int64_t ld, int32_t k) {
     pl.ok = true;
     return pl;
   }
-  for (int chunk : {8192, kTopkMaxChunk}) {
+  for (int chunk : {4096, 8192, kTopkMaxChunk}) {
     const int64_t n = ceil_div(ld, chunk);
     if (n * k <= kTopkMaxCand) {
       pl.chunk = chunk;
@@ -201,6 +201,12 @@ size_t csa_attn_workspace_size(int32_t n_queries, int32_t H, int32_t D_nope, int
 }
 
 static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t workspace_bytes, void* stream) {
+  const float smax = std::max(p.lat_scale, p.swa_scale);
+  const float pmul = std::ldexp(1.0f, 8 - kAttnTau);
+  p.sm_log2 = p.sm_scale * 1.4426950408889634f;
+  p.pscale_lat = p.lat_scale / smax * pmul;
+  p.pscale_swa = p.swa_scale / smax * pmul;
+  p.nope_unit = smax / pmul;
   AttnPlan pl;
   const size_t avail = (workspace && aligned16(workspace)) ? workspace_bytes : 0;
   if (!plan_attn(p.T, p.H, p.D_nope + p.D_rope, max_slots, avail, true, &pl)) return CSA_ERR_WORKSPACE;
@@ -208,7 +214,7 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
   p.n_splits = pl.n_splits;
   p.per_split = pl.per_split;
   p.part = pl.n_splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  const int64_t blocks = ceil_div(p.T, 8) * 8 * (int64_t)p.n_hg * p.n_splits;
+  const int64_t blocks = (p.T >= 8 ? ceil_div(p.T, 8) * 8 : (int64_t)p.T) * p.n_hg * p.n_splits;
   if (blocks >= ((int64_t)1 << 31)) return CSA_ERR_UNSUPPORTED;
   return launch_status(launch_attn(p, (hipStream_t)stream));
 }

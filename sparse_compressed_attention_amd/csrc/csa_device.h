@@ -68,12 +68,13 @@ __device__ __forceinline__ float max_over_groups(float x) {
 }
 
 // ---- number formats ------------------------------------------------------
-// Round-to-nearest-even FP32 -> BF16 bits (finite inputs; NaN kept quiet).
+// Round-to-nearest-even FP32 -> BF16 bits, branch-free; NaN stays a quiet
+// NaN, infinities stay infinities.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const bool nan = (u & 0x7fffffffu) > 0x7f800000u;
+  return (uint16_t)(nan ? ((u >> 16) | 0x40u) : rounded);
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 

@@ -60,6 +60,10 @@ struct AttnParams {
   float* part;             // [n_splits][T][H][D + 2] or nullptr
   float lat_scale, swa_scale;
   float sm_scale;          // softmax scale (natural-log units)
+  // derived on the host (uniform): sm_scale*log2(e); FP8 probability scale
+  // per key source (key scale / max scale * 2^(8 - tau)); value unit of the
+  // FP8 accumulator (max scale / 2^(8 - tau))
+  float sm_log2, pscale_lat, pscale_swa, nope_unit;
   int num_pages, page_size, max_pages, ratio_m;
   int k, W;
   int prefill_seq;         // -1: decode (query t belongs to sequence t)
@@ -70,6 +74,7 @@ struct AttnParams {
 };
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
 constexpr int kAttnMaxSlots = 2048;   // key slots one workgroup handles
+constexpr int kAttnTau = 4;           // lazy-rescale threshold (log2 units)
 constexpr int kAttnTile = 64;
 
 }  // namespace csa

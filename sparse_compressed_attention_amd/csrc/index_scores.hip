@@ -7,13 +7,17 @@
 // tensor units in FP8 over every visible compressed entry.
 //
 // Mapping on gfx950: one workgroup (4 waves) scores one query row over a
-// chunk of entries.  Per 16 entries a wave runs one v_mfma 16x16x128 FP8
-// per 16 index heads: A = the query's index heads (rows) x 128 dims, held in
-// registers for the whole chunk; B = 16 entry keys x 128 dims, loaded
-// straight from HBM into the operand registers (each key byte is used once,
-// so no LDS staging).  The ReLU, the head weights and the reduction over
-// heads stay in registers; the head reduction crosses the four 16-lane
-// groups with two permlane swaps.  The scan is HBM-bound (128 FLOP/byte).
+// chunk of 1024 entries; each wave owns 256 consecutive entries = 16 groups
+// of 16.  Per group a wave runs one v_mfma 16x16x128 FP8 per 16 index heads:
+// A = the query's index heads (rows) x 128 dims, held in registers for the
+// whole chunk; B = 16 entry keys x 128 dims, loaded straight from HBM into
+// the operand registers (each key byte is used once, so no LDS staging).
+// The pages of the wave's 16 groups come from one vector load (lane u
+// fetches group u's page id; a group of 16 never straddles a page because the
+// page size is a multiple of 16), then all 16 groups' key loads are issued
+// before the first MFMA (32 KB in flight per wave, two waves per SIMD).  The ReLU, the head weights and the reduction over heads stay in
+// registers; the head reduction crosses the four 16-lane groups with two
+// permlane swaps.  The scan is HBM-bound (128 FLOP/byte).
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -22,13 +26,15 @@ namespace csa {
 namespace {
 
 constexpr int kIdxWaves = 4;
-constexpr int kIdxUnroll = 8;   // groups of 16 entries in flight per wave
+constexpr int kIdxGroups = 16;                       // groups of 16 entries per wave
+constexpr int kIdxWaveEntries = 16 * kIdxGroups;     // 256
+constexpr int kIdxChunk = kIdxWaves * kIdxWaveEntries;
 
-__global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p) {
+__global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexParams p) {
   const int t = blockIdx.x / p.n_chunks;
   const int chunk = blockIdx.x - t * p.n_chunks;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r = lane & 15;
 
@@ -38,13 +44,45 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p) {
   if (seq >= 0 && seq < p.B && pos >= 0) nv = min(pos / p.ratio_m, p.n_comp[seq]);
   nv = max(0, min(nv, (int)min<int64_t>(p.ld, 0x7fffffff)));
   if (chunk == 0 && threadIdx.x == 0) p.n_visible[t] = nv;
-  const int c0 = chunk * p.chunk;
-  if (c0 >= nv) return;
-  const int c1 = min(nv, c0 + p.chunk);
+  const int e_begin = chunk * kIdxChunk + wave * kIdxWaveEntries;
+  if (e_begin >= nv) return;
+  const int e_end = min(nv, e_begin + kIdxWaveEntries);
+
+  // Page of every group first (lane u < 16 fetches group u's page id: one
+  // round trip), then all key loads back to back.  Group u covers entries
+  // e_begin + 16 u + (0..15); lane (g, r) loads entry r's dims [32g, 32g+32).
+  const bool dim_ok = 32 * g < p.D_I;
+  const int32_t* pt = p.page_table + (size_t)seq * p.max_pages;
+  int my_page = -1;
+  {
+    const int e0 = e_begin + 16 * lane;
+    if (lane < kIdxGroups && e0 < e_end) {
+      const int pi = e0 / p.page_size;
+      if (pi < p.max_pages) my_page = pt[pi];
+    }
+  }
+  int poff = e_begin % p.page_size;        // uniform: offset of group u in its page
+  v8i kb[kIdxGroups];
+  uint32_t ok_mask = 0;                    // uniform: group has a valid page
+#pragma unroll
+  for (int u = 0; u < kIdxGroups; ++u) {
+    const int e0 = e_begin + 16 * u;
+    const int page = __builtin_amdgcn_readlane(my_page, u);
+    const bool ok = e0 < e_end && page >= 0 && page < p.num_pages;
+    ok_mask |= (ok ? 1u : 0u) << u;
+    v8i x = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    if (ok && dim_ok && e0 + r < e_end) {
+      const uint8_t* src = p.k_idx + ((size_t)page * p.page_size + poff + r) * p.D_I + 32 * g;
+      const v4i lo = ld16(src), hi = ld16(src + 16);
+      x = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    kb[u] = x;
+    poff += 16;
+    if (poff >= p.page_size) poff -= p.page_size;
+  }
 
   // Query operand: 4 tiles of 16 index heads; lane holds head 16*ht + r,
   // dims [32g, 32g+32).  Weights for output rows (heads 16*ht + 4g + i).
-  const bool dim_ok = 32 * g < p.D_I;
   v8i qa[4];
   float wv[4][4];
 #pragma unroll
@@ -52,7 +90,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p) {
     const int h = 16 * ht + r;
     if (h < p.H_I && dim_ok) {
       const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
-      v4i lo = ld16(src), hi = ld16(src + 16);
+      const v4i lo = ld16(src), hi = ld16(src + 16);
       qa[ht] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else {
       qa[ht] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
@@ -60,46 +98,26 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = 16 * ht + 4 * g + i;
-      wv[ht][i] = hh < p.H_I ? p.w[(size_t)t * p.H_I + hh] : 0.0f;
+      wv[ht][i] = hh < p.H_I ? p.w[(size_t)t * p.H_I + hh] * p.qk_scale : 0.0f;
     }
   }
   const int n_ht = (p.H_I + 15) >> 4;
 
-  const int32_t* pt = p.page_table + (size_t)seq * p.max_pages;
   float* out = p.scores + (size_t)t * p.ld;
-  const int step = 16 * kIdxUnroll * kIdxWaves;
-  for (int e0 = c0 + 16 * kIdxUnroll * wave; e0 < c1; e0 += step) {
-    v8i kb[kIdxUnroll];
-    bool ok[kIdxUnroll];
 #pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
-      const int e = e0 + 16 * u + r;
-      int page = -1;
-      if (e < c1 && e / p.page_size < p.max_pages) page = pt[e / p.page_size];
-      ok[u] = page >= 0 && page < p.num_pages;
-      if (ok[u] && dim_ok) {
-        const uint8_t* src = p.k_idx + ((size_t)page * p.page_size + (e % p.page_size)) * p.D_I + 32 * g;
-        v4i lo = ld16(src), hi = ld16(src + 16);
-        kb[u] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      } else {
-        kb[u] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+  for (int u = 0; u < kIdxGroups; ++u) {
+    const int e = e_begin + 16 * u + r;
+    float part = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      if (ht < n_ht) {
+        const v4f acc = mfma_f8_128(qa[ht], kb[u], (v4f){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.0f);
       }
     }
-#pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
-      float part = 0.0f;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        if (ht < n_ht) {
-          v4f acc = mfma_f8_128(qa[ht], kb[u], (v4f){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.0f);
-        }
-      }
-      part = sum_over_groups(part);
-      const int e = e0 + 16 * u + r;
-      if (g == 0 && e < c1) out[e] = ok[u] ? part * p.qk_scale : -__builtin_inff();
-    }
+    part = sum_over_groups(part);
+    if (g == 0 && e < e_end) out[e] = ((ok_mask >> u) & 1u) ? part : -__builtin_inff();
   }
 }
 
@@ -111,6 +129,6 @@ hipError_t launch_index_scores(const IndexParams& p, hipStream_t stream) {
   return hipPeekAtLastError();
 }
 
-int index_chunk_entries() { return 16 * kIdxUnroll * kIdxWaves * 2; }
+int index_chunk_entries() { return kIdxChunk; }
 
 }  // namespace csa

@@ -184,3 +184,53 @@ def test_deterministic_repeat():
     b = run_gpu(wl)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
+
+
+# --------------------------------------------------------------- top-k kernel alone
+@pytest.mark.parametrize("k", [1, 16, 512, 2048])
+def test_topk_kernel_exact_on_synthetic_rows(k):
+    """csa_topk against the selection rule (index work: bit-exact), on rows
+    with heavy ties, all-equal values, +-0, -inf and lengths around k and
+    around the 16384-entry chunk, including rows that need the second stage."""
+    say(f"case topk kernel k={k}")
+    rng = np.random.default_rng(k)
+    lens = [0, 1, k - 1 if k > 1 else 1, k, k + 1, 3000, 8191, 16384, 16385, 40000, 131071]
+    kinds = ["normal", "ties", "equal", "zeros", "neginf"]
+    ld = max(lens)
+    rows, nvis = [], []
+    for i, n in enumerate(lens):
+        kind = kinds[i % len(kinds)]
+        if kind == "normal":
+            v = rng.standard_normal(n).astype(np.float32)
+        elif kind == "ties":
+            v = rng.integers(0, 10, size=n).astype(np.float32)
+        elif kind == "equal":
+            v = np.full(n, 3.5, dtype=np.float32)
+        elif kind == "zeros":
+            v = np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+            v[rng.random(n) < 0.01] = 1.0
+        else:
+            v = rng.standard_normal(n).astype(np.float32)
+            v[rng.random(n) < 0.3] = -np.inf
+        row = np.full(ld, np.nan, dtype=np.float32)   # columns past n_visible must never be read
+        row[:n] = v
+        rows.append(row)
+        nvis.append(n)
+    scores = torch.from_numpy(np.stack(rows)).cuda()
+    nv = torch.tensor(nvis, dtype=torch.int32).cuda()
+    out = torch.full((len(lens), k), 7777, dtype=torch.int32).cuda()
+    ws_n = csa.csa_topk_workspace_size(len(lens), ld, k)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8).cuda() if ws_n else None
+    csa.csa_topk(scores, nv, k, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i, n in enumerate(lens):
+        want = oracle.topk_select(rows[i][:n].astype(np.float64), k)
+        assert np.array_equal(got[i], want), (k, n, kinds[i % len(kinds)])
+
+
+@pytest.mark.parametrize("page_size", [16, 48, 64, 96])
+def test_indexer_page_sizes(page_size):
+    say(f"case indexer page {page_size}")
+    spec = ci.small_spec(ctx_lens=[4000, 1508, 2900], shuffle_pages=True, page_size=page_size)
+    check_full(ci.generate(spec, seed=200 + page_size))
