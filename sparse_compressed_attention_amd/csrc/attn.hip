@@ -16,9 +16,15 @@
 // Mapping on gfx950 (256 threads = 4 waves per workgroup):
 //  * a workgroup owns one query, 32 heads and a range of key slots (the range
 //    is split over workgroups only when there are few queries);
-//  * wave (ht, kh): heads [16 ht, 16 ht + 16) of the group; within every
-//    64-key tile it takes keys [32 kh, 32 kh + 32).  The two kh waves of a head
-//    tile merge their softmax states through LDS at the end;
+//  * wave (ht, dh): heads [16 ht, 16 ht + 16) of the group and one half of
+//    the latent dims (dh = 0: the first nope blocks; dh = 1: the remaining
+//    nope dims and the rope dims).  Every 64-key tile is handled whole by
+//    both waves of a head tile: each computes the scores over its own dims,
+//    the two partial score tiles are added through LDS, both run the same
+//    online softmax (bit-identical state), and each accumulates O for its
+//    own dims only.  O and q of a wave are half of a head tile's, which
+//    keeps a wave's registers small, and no merge of softmax states is
+//    needed at the end;
 //  * gather: key descriptors (top-k index -> page table -> row, or window slot
 //    -> row) are resolved once into LDS; each 64-key tile is copied from HBM
 //    straight into LDS with global_load_lds_dwordx4 (no register staging),
@@ -26,22 +32,24 @@
 //    tile is stored as "planes": plane c holds the c-th 16-byte chunk of all
 //    64 rows, so one DMA instruction writes one whole plane and every lane
 //    keeps one row (key) for all of its DMAs.  Rows 16..31 and 48..63 are
-//    XOR-swizzled by 4 slots so that the transpose reads below never hit the
-//    same LDS banks.  The cache's FP8/BF16 bytes go to the MFMA unchanged;
+//    XOR-swizzled by 4 slots against LDS bank conflicts of the transpose
+//    reads.  Rows of masked keys (padding, invalid entries, the ragged tail)
+//    are cleared in LDS once their DMA has landed, so no operand needs a
+//    per-key mask.  The cache's FP8/BF16 bytes go to the MFMA unchanged;
 //  * QK: S^T (keys x heads) = X . Q^T on v_mfma 16x16x128 FP8, with q split
 //    into two E4M3 terms hi + lo sharing a power-of-two per-head scale (the K
 //    dimension is [hi | lo], X read once and used for both), plus the rope
-//    dims on v_mfma 16x16x32 BF16; the two 16-key subtiles are interleaved
-//    and the next X operands are read from LDS before the current MFMAs;
-//  * online softmax in FP32, exp2 domain; each lane owns one head, so the
-//    rescale of O needs no cross-lane traffic.  The running max is raised
-//    lazily: only when a tile's max exceeds it by more than 2^tau (tau = 4),
-//    so probabilities stay <= 2^tau and the O rescale runs on few tiles.  The
-//    sink starts the running max and denominator (zero value);
-//  * PV: O^T (dims x heads) += X^T . P^T: X^T is read from the same LDS tile
-//    with ds_read_b64_tr_b8 (nope, FP8; P as two E4M3 terms hi + lo after a
-//    2^(8 - tau) scale) and ds_read_b64_tr_b16 (rope, BF16, P in BF16); bytes
-//    of masked keys are cleared in registers; P never leaves registers.
+//    dims on v_mfma 16x16x32 BF16; four 16-key subtiles in flight;
+//  * online softmax in FP32, exp2 domain; each lane owns one head.  The
+//    running max is raised lazily: only when a tile's max exceeds it by more
+//    than 2^tau (tau = 4), so probabilities stay <= 2^tau and the O rescale
+//    runs on few tiles.  The sink starts the running max and denominator;
+//  * PV: O^T (dims x heads) += X^T . P^T on v_mfma 16x16x128 FP8 with
+//    K = [64 keys, P hi | 64 keys, P lo] (P x key-scale ratio x 2^(8 - tau)
+//    as two E4M3 terms); X^T comes from the same LDS tile through
+//    ds_read_b64_tr_b8 (two reads per 16 dims, used for both terms).  Rope
+//    dims use ds_read_b64_tr_b16 and v_mfma 16x16x32 BF16 with P in BF16.
+//    P never leaves registers.
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -55,27 +63,40 @@ constexpr int kPlane = kAttnTile * 16;   // bytes per plane (64 rows x 16 B)
 
 template <int DN, int DR>
 struct Cfg {
-  static constexpr int NFB = DN / 128;                                       // full 128-dim blocks
-  static constexpr int REM = DN % 128;                                       // combined hi|lo block
-  static constexpr int NR = (DR + 31) / 32;                                  // rope k-steps
-  static constexpr int ND = DN / 16;                                         // PV nope dim tiles
-  static constexpr int NDR = DR / 16;                                        // PV rope dim tiles
-  static constexpr int NDT = ND + NDR;
-  static constexpr int HALF = NDT / 2;
-  static constexpr int CHN = DN / 16;                                        // nope planes
-  static constexpr int CHR = 2 * DR / 16;                                    // rope planes
+  static constexpr int NFB = DN / 128;                       // full 128-dim nope blocks
+  static constexpr int REM = DN % 128;                       // combined hi|lo block (<= 64 dims)
+  static constexpr int NBLK = NFB + (REM > 0 ? 1 : 0);
+  static constexpr int B0 = (NBLK + 1) / 2;                  // nope blocks of dim half 0
+  static constexpr int N0 = DN < 128 * B0 ? DN : 128 * B0;   // nope dims of dim half 0
+  static constexpr int CHN = DN / 16;                        // nope planes
+  static constexpr int CHR = DR / 8;                         // rope planes
   static constexpr int CH = CHN + CHR;
-  static constexpr int PPW = (CH + 3) / 4;                                   // planes per wave (max)
-  static constexpr int PMIN = CH / 4;                                        // planes per wave (min)
+  static constexpr int PPW = (CH + 3) / 4;                   // planes per wave (max)
+  static constexpr int PMIN = CH / 4;                        // planes per wave (min)
   static constexpr int TILE_BYTES = CH * kPlane;
   static_assert(DN % 16 == 0 && DR % 16 == 0, "dims must be multiples of 16");
   static_assert(REM <= 64, "remainder block must fit one combined hi|lo MFMA");
-  static_assert(NDT % 2 == 0, "dim tiles split evenly between the two key halves");
   static_assert(PMIN >= 1, "every wave issues at least one plane per tile");
 };
 
-// key (0..31) of this wave's half-tile held by byte e (0..7) of a lane in
-// 16-lane group g, as produced by the QK output layout of two 16-key subtiles.
+// What dim half DH of a head tile owns.
+template <int DN, int DR, int DH>
+struct Half {
+  using C = Cfg<DN, DR>;
+  static constexpr int FB = DH == 0 ? (C::B0 < C::NFB ? C::B0 : C::NFB) : (C::NFB > C::B0 ? C::NFB - C::B0 : 0);
+  static constexpr int FB0 = DH == 0 ? 0 : C::B0;           // first full block
+  static constexpr bool COMB = C::REM > 0 && ((C::NFB < C::B0) == (DH == 0));
+  static constexpr int NR = DH == 1 ? (DR + 31) / 32 : 0;    // rope k-steps of QK
+  static constexpr int PT0 = DH == 0 ? 0 : C::N0 / 16;       // first nope dim tile of PV
+  static constexpr int NPT = DH == 0 ? C::N0 / 16 : C::CHN - C::N0 / 16;
+  static constexpr int NRT = DH == 1 ? DR / 16 : 0;          // rope dim tiles of PV
+  static constexpr int NO = NPT + NRT;                       // O accumulators
+  static constexpr int NQB = FB + (COMB ? 1 : 0);
+  static_assert(NO >= 1, "every dim half owns output dims");
+};
+
+// key (0..31) held by byte e (0..7) of a lane in 16-lane group g: the keys
+// of the two 16-key subtiles that the QK output layout puts in that lane.
 __device__ __forceinline__ int kappa(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
 // LDS slot of key k inside a plane (an involution).
 __device__ __forceinline__ int slot_of(int k) { return k ^ (((k >> 4) & 1) << 2); }
@@ -87,76 +108,77 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-template <int DN, int DR>
-__global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt(0)) but leaves the tile DMAs in flight, unlike __syncthreads,
+// which also drains vmcnt.  The empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt unchanged
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One global_load_lds_dwordx4: every lane copies 16 bytes from `src` to LDS
+// byte address lds_base + 16 * lane.  Issued through asm so that the
+// compiler's wait-count pass does not see an LDS write in flight: left to
+// itself it drains vmcnt before every later LDS access, which would wait for
+// the prefetched tiles too.  The kernel orders these copies itself (wait_vmcnt
+// + barrier before a tile is read; a buffer is refilled only after the
+// barrier that follows its last read).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ int page_div(int n, const AttnParams& p) {
+  return (int)(((uint64_t)(uint32_t)n * p.ps_magic) >> p.ps_shift);
+}
+
+struct Block {
+  int t, hg, split, seq;
+  int pos, nc;
+  int n_sel, sel_end, kv0, nkeys;   // slots: [0, n_sel) selected, [sel_end, sel_end + W) window
+};
+
+template <int DN, int DR, int DH>
+__device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, uint8_t* xs0, int32_t* desc,
+                                          v4f* sx, int wave) {
   using C = Cfg<DN, DR>;
+  using HF = Half<DN, DR, DH>;
   constexpr int D = DN + DR;
-
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf][C::TILE_BYTES];
-  __shared__ int32_t desc[kAttnMaxSlots];
-
-  // ---- which (query, head group, split).  Workgroups go to the 8 XCDs
-  // round-robin by id.  With 8 or more queries, queries are spread over the
-  // XCDs and all workgroups of one query share an XCD (and its L2, which then
-  // serves the head groups' repeated reads of the same rows); with fewer,
-  // a query's workgroups are spread over all XCDs instead.
-  const int nb = p.n_hg * p.n_splits;
-  const int bid = blockIdx.x;
-  int t, jb;
-  if (p.T >= 8) {
-    const int local = bid >> 3;
-    t = (local / nb) * 8 + (bid & 7);
-    jb = local % nb;
-  } else {
-    t = bid / nb;
-    jb = bid - t * nb;
-  }
-  if (t >= p.T) return;
-  const int hg = jb / p.n_splits;
-  const int split = jb - hg * p.n_splits;
-
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r = lane & 15;
   const int ht = wave & 1;
-  const int kh = wave >> 1;
-  const int h = hg * 32 + ht * 16 + r;
-  const bool tile_ok = hg * 32 + ht * 16 < p.H;
+  const int h = bk.hg * 32 + ht * 16 + r;
+  const bool tile_ok = bk.hg * 32 + ht * 16 < p.H;
   const bool head_ok = h < p.H;
   const bool prefill = p.prefill_seq >= 0;
-  const int seq = prefill ? p.prefill_seq : t;
-  const int pos = p.q_pos[t];
-  const int nc = p.n_comp[seq];
-  const int nv = pos >= 0 ? max(0, min(pos / p.ratio_m, nc)) : 0;
-  const int n_sel = p.topk ? p.k : nv;
-  const int n_slots = n_sel + p.W;
-  const int kv0 = split * p.per_split;
-  if (split > 0 && kv0 >= n_slots) return;   // empty split: the merge skips it
-  const int kv1 = min(n_slots, kv0 + p.per_split);
-  const int nkeys = max(0, kv1 - kv0);
+  const int t = bk.t, seq = bk.seq, kv0 = bk.kv0, nkeys = bk.nkeys, n_sel = bk.n_sel, sel_end = bk.sel_end;
 
-  // ---- query rows: loads issued first (packed BF16, 64 VGPRs) so their
-  // latency overlaps the descriptor round trips; converted after the first
-  // tile DMAs are issued
-  v4i qraw[C::NFB + 1][4];
-  v4i qrope[C::NR];
+  // ---- query rows of this dim half (packed BF16), issued first so that
+  // their latency overlaps the descriptor round trips
+  v4i qraw[HF::NQB > 0 ? HF::NQB : 1][4];
+  v4i qrope[HF::NR > 0 ? HF::NR : 1];
   {
     const uint16_t* qrow = p.q + (size_t)t * p.q_stride + (size_t)h * D;
 #pragma unroll
-    for (int b = 0; b <= C::NFB; ++b) {
-      const bool comb = (b == C::NFB);
-      const int d0 = comb ? 128 * C::NFB + 32 * (g & 1) : 128 * b + 32 * g;
+    for (int b = 0; b < HF::NQB; ++b) {
+      const bool comb = b == HF::FB;
+      const int d0 = comb ? 128 * C::NFB + 32 * (g & 1) : 128 * (HF::FB0 + b) + 32 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int dd = d0 + 8 * c;
         v4i raw = (v4i){0, 0, 0, 0};
-        if (head_ok && (!comb || C::REM > 0) && dd < DN) raw = ld16(qrow + dd);
+        if (head_ok && dd < DN) raw = ld16(qrow + dd);
         qraw[b][c] = raw;
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < C::NR; ++rr) {
+    for (int rr = 0; rr < HF::NR; ++rr) {
       const int dd = 32 * rr + 8 * g;
       v4i raw = (v4i){0, 0, 0, 0};
       if (head_ok && dd < DR) raw = ld16(qrow + DN + dd);
@@ -166,8 +188,8 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
   const float sink_raw = head_ok ? p.sink[h] : 0.0f;
 
   // ---- key descriptors of this workgroup's slots: row | source flag, -1 =
-  // skip.  All first-level loads (top-k index or ring position) are issued
-  // together, then all page-table loads: two round trips in total.
+  // skip.  First-level loads (top-k index or ring position) need nothing
+  // loaded before them; then all page-table loads: two round trips.
   const int32_t* pt = p.page_table + (size_t)seq * p.max_pages;
   constexpr int kSPT = kAttnMaxSlots / 256;   // slots per thread
   int v1[kSPT];
@@ -179,8 +201,8 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
     if (s < nkeys) {
       if (slot < n_sel) {
         v = p.topk ? p.topk[(size_t)t * p.k + slot] : slot;
-      } else if (!prefill) {
-        v = p.swa_pos[(size_t)seq * p.W + (slot - n_sel)];
+      } else if (slot >= sel_end && !prefill) {
+        v = p.swa_pos[(size_t)seq * p.W + (slot - sel_end)];
       }
     }
     v1[j] = v;
@@ -189,13 +211,15 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int j = 0; j < kSPT; ++j) {
     const int s = threadIdx.x + 256 * j;
-    const int slot = kv0 + s;
     const int idx = v1[j];
     int page = -1;
-    if (s < nkeys && slot < n_sel && idx >= 0 && idx < nc && idx / p.page_size < p.max_pages)
-      page = pt[idx / p.page_size];
+    if (s < nkeys && kv0 + s < n_sel && idx >= 0) {
+      const int pi = page_div(idx, p);
+      if (pi < p.max_pages) page = pt[pi];
+    }
     v2[j] = page;
   }
+  const int pos = bk.pos;
 #pragma unroll
   for (int j = 0; j < kSPT; ++j) {
     const int s = threadIdx.x + 256 * j;
@@ -204,9 +228,10 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
     int d = -1;
     if (slot < n_sel) {
       const int idx = v1[j], page = v2[j];
-      if (page >= 0 && page < p.num_pages) d = page * p.page_size + idx % p.page_size;
-    } else {
-      const int jw = slot - n_sel;
+      if (idx < bk.nc && page >= 0 && page < p.num_pages)
+        d = page * p.page_size + (idx - page_div(idx, p) * p.page_size);
+    } else if (slot >= sel_end) {
+      const int jw = slot - sel_end;
       if (!prefill) {
         const int pp = v1[j];
         if (pp >= 0 && pp <= pos && pp > pos - p.W) d = (seq * p.W + jw) | kSwaFlag;
@@ -223,9 +248,12 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
 
   // ---- tile DMA: lane -> the key whose plane slot is `lane`, planes
   // c = wave + 4 i.  Masked keys copy a dummy row (row 0) so that every wave
-  // issues the same number of DMAs per tile; their bytes are never used.
+  // issues the same number of DMAs per tile; those rows are cleared in LDS
+  // before use.
   const int dkey = slot_of(lane);
-  auto issue_tile = [&](int tile, int buf) {
+  constexpr int kParts = 3;                          // a tile's DMAs go out in three parts
+  constexpr int kPerPart = (C::PPW + kParts - 1) / kParts;
+  auto issue_tile = [&](int tile, int buf, int part) {
     const int s = tile * kAttnTile + dkey;
     const int d = s < nkeys ? desc[s] : -1;
     const uint8_t* nsrc = p.lat_nope;
@@ -240,26 +268,25 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
         rsrc = reinterpret_cast<const uint8_t*>(p.lat_rope + row * DR);
       }
     }
-    uint8_t* base = xs[buf];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(CSA_LDS uint8_t*)(xs0 + buf * C::TILE_BYTES);
 #pragma unroll
     for (int i = 0; i < C::PPW; ++i) {
       const int c = wave + 4 * i;
-      if (c < C::CH) {
+      if (c < C::CH && (part < 0 || i / kPerPart == part)) {
         const uint8_t* src = (c < C::CHN) ? nsrc + 16 * c : rsrc + 16 * (c - C::CHN);
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                         (void CSA_LDS*)(base + c * kPlane), 16, 0, 0);
+        dma16(src, lds_base + c * kPlane);
       }
     }
   };
 
   const int n_tiles = (nkeys + kAttnTile - 1) / kAttnTile;
-  if (n_tiles > 0) issue_tile(0, 0);
-  if (n_tiles > 1) issue_tile(1, 1);
+  if (n_tiles > 0) issue_tile(0, 0, -1);
+  if (n_tiles > 1) issue_tile(1, 1, -1);
 
   // ---- query operands: q split into two E4M3 terms hi + lo with a shared
-  // power-of-two per-head scale (registers for the whole kernel)
-  v8i qhi[C::NFB > 0 ? C::NFB : 1], qlo[C::NFB > 0 ? C::NFB : 1], qcomb;
-  v8bf qr[C::NR];
+  // power-of-two per-head scale over this half's nope dims
+  v8i qhi[HF::FB > 0 ? HF::FB : 1], qlo[HF::FB > 0 ? HF::FB : 1], qcomb;
+  v8bf qr[HF::NR > 0 ? HF::NR : 1];
   float cq = 0.0f;
   const float cr = p.sm_log2;
   {
@@ -269,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
     };
     float amax = 0.0f;
 #pragma unroll
-    for (int b = 0; b <= C::NFB; ++b)
+    for (int b = 0; b < HF::NQB; ++b)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -279,7 +306,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
     const float inv = 1.0f / s;
     cq = head_ok ? cr * s : 0.0f;
 #pragma unroll
-    for (int b = 0; b <= C::NFB; ++b) {
+    for (int b = 0; b < HF::NQB; ++b) {
       v8i hi, lo;
 #pragma unroll
       for (int w4 = 0; w4 < 8; ++w4) {
@@ -292,7 +319,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
         hi[w4] = hw;
         lo[w4] = pack4_fp8(res[0], res[1], res[2], res[3]);
       }
-      if (b < C::NFB) {
+      if (b < HF::FB) {
         qhi[b] = hi;
         qlo[b] = lo;
       } else {
@@ -300,276 +327,351 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < C::NR; ++rr) qr[rr] = __builtin_bit_cast(v8bf, qrope[rr]);
+    for (int rr = 0; rr < HF::NR; ++rr) qr[rr] = __builtin_bit_cast(v8bf, qrope[rr]);
   }
-  if (C::NFB == 0) {
-    qhi[0] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-    qlo[0] = qhi[0];
-  }
+  const float cql = cq * p.lat_scale, cqs = cq * p.swa_scale;
 
-  // ---- softmax state (exp2 domain); only one wave per head carries the sink
-  const bool sink_here = split == 0 && kh == 0 && head_ok;
+  // ---- softmax state (exp2 domain), identical in both dim halves
+  const bool sink_here = bk.split == 0 && head_ok;
   const float sink2 = head_ok ? sink_raw * kLog2e : -__builtin_inff();
   float m_run = sink_here ? sink2 : -__builtin_inff();
   float l_run = (sink_here && g == 0 && sink2 > -__builtin_inff()) ? 1.0f : 0.0f;
-  v4f O[C::NDT];
+  v4f O[HF::NO];
 #pragma unroll
-  for (int i = 0; i < C::NDT; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < HF::NO; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+  // loop-invariant LDS byte offsets
+  int qk_row[4];                                      // QK: key 16 st + r
+#pragma unroll
+  for (int st = 0; st < 4; ++st) qk_row[st] = 16 * slot_of(16 * st + r);
+  const int pv0 = 16 * slot_of(kappa(g, r >> 1)) + 8 * (r & 1);        // tr8 rows, keys 0..31
+  const int pv1 = 16 * slot_of(32 + kappa(g, r >> 1)) + 8 * (r & 1);   // keys 32..63
+  const int rp_pl = C::CHN + ((r >> 1) & 1);
+  const int rp0 = rp_pl * kPlane + 16 * slot_of(kappa(g, r >> 2)) + 8 * (r & 1);
+  const int rp1 = rp_pl * kPlane + 16 * slot_of(kappa(g, 4 + (r >> 2))) + 8 * (r & 1);
+  const int rp2 = rp_pl * kPlane + 16 * slot_of(32 + kappa(g, r >> 2)) + 8 * (r & 1);
+  const int rp3 = rp_pl * kPlane + 16 * slot_of(32 + kappa(g, 4 + (r >> 2))) + 8 * (r & 1);
+  v4f* sx_own = sx + (size_t)wave * 4 * 64 + lane;
+  const v4f* sx_oth = sx + (size_t)(wave ^ 2) * 4 * 64 + lane;
 
-  const int sl_q0 = slot_of(32 * kh + r);          // QK rows of subtile 0 / 1
-  const int sl_q1 = slot_of(32 * kh + 16 + r);
   int buf = 0;
   for (int it = 0; it < n_tiles; ++it, buf = (buf + 1 == kNBuf) ? 0 : buf + 1) {
     // tile `it` landed in LDS (this wave's DMAs), then everyone's (barrier);
     // the barrier also retires every wave's reads of the buffer reused next
+    asm volatile("" ::: "memory");
     if (it + 1 < n_tiles) wait_vmcnt<C::PMIN>(); else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (it + 2 < n_tiles) issue_tile(it + 2, buf == 0 ? 2 : buf - 1);
-    if (!tile_ok) continue;
-    const uint8_t* xb = xs[buf];
+    asm volatile("" ::: "memory");
+    const bool refill = it + 2 < n_tiles;
+    const int nbuf = buf == 0 ? 2 : buf - 1;
+    if (refill) issue_tile(it + 2, nbuf, 0);
+    uint8_t* xb = xs0 + buf * C::TILE_BYTES;
 
-    // -- QK for the wave's two 16-key subtiles, interleaved
-    auto xread = [&](int sl, int c0) -> v8i {
-      const v4i lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + 16 * sl);
-      const v4i hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + 16 * sl);
-      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    auto xcomb = [&](int sl) -> v8i {
-      const int c0 = 8 * C::NFB + 2 * (g & 1);
-      v8i x = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-      if (32 * (g & 1) < C::REM) {
-        const v4i lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + 16 * sl);
-        v4i hi = (v4i){0, 0, 0, 0};
-        if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + 16 * sl);
-        x = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      return x;
-    };
-    v4f a0 = (v4f){0.f, 0.f, 0.f, 0.f}, a1 = a0;
-    v8i x0, x1;
-    if (C::NFB > 0) {
-      x0 = xread(sl_q0, 2 * g);
-      x1 = xread(sl_q1, 2 * g);
-    } else {
-      x0 = xcomb(sl_q0);
-      x1 = xcomb(sl_q1);
-    }
+    // -- valid keys of the tile (the same in every wave): bit k = key k.
+    //    Rows of masked keys are cleared, so they add nothing to S or O.
+    const int sk = it * kAttnTile + lane;
+    const int dk = sk < nkeys ? desc[sk] : -1;
+    const uint64_t vmask = __ballot(dk >= 0);
+    const bool full = vmask == ~0ull;
+    if (!full) {
+      if (dk < 0) {
 #pragma unroll
-    for (int b = 0; b < C::NFB; ++b) {
-      v8i n0, n1;
-      if (b + 1 < C::NFB) {
-        n0 = xread(sl_q0, 8 * (b + 1) + 2 * g);
-        n1 = xread(sl_q1, 8 * (b + 1) + 2 * g);
-      } else {
-        n0 = xcomb(sl_q0);
-        n1 = xcomb(sl_q1);
-      }
-      a0 = mfma_f8_128(x0, qhi[b], a0);
-      a1 = mfma_f8_128(x1, qhi[b], a1);
-      a0 = mfma_f8_128(x0, qlo[b], a0);
-      a1 = mfma_f8_128(x1, qlo[b], a1);
-      x0 = n0;
-      x1 = n1;
-    }
-    if (C::REM > 0) {
-      a0 = mfma_f8_128(x0, qcomb, a0);
-      a1 = mfma_f8_128(x1, qcomb, a1);
-    }
-    v4f r0 = (v4f){0.f, 0.f, 0.f, 0.f}, r1 = r0;
-#pragma unroll
-    for (int rr = 0; rr < C::NR; ++rr) {
-      const int c = C::CHN + 4 * rr + g;
-      v4i y0 = (v4i){0, 0, 0, 0}, y1 = y0;
-      if (32 * rr + 8 * g < DR) {
-        y0 = *reinterpret_cast<const v4i*>(xb + c * kPlane + 16 * sl_q0);
-        y1 = *reinterpret_cast<const v4i*>(xb + c * kPlane + 16 * sl_q1);
-      }
-      r0 = mfma_bf16_32(__builtin_bit_cast(v8bf, y0), qr[rr], r0);
-      r1 = mfma_bf16_32(__builtin_bit_cast(v8bf, y1), qr[rr], r1);
-    }
-
-    // -- online softmax (lane: head h, keys kappa(g, e) of this half-tile)
-    float sv[8], kq[8];
-    uint32_t m8lo = 0, m8hi = 0;   // byte masks of the valid keys (PV operands)
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int st = e >> 2, i = e & 3;
-      const int s = it * kAttnTile + 32 * kh + 16 * st + 4 * g + i;   // = key kappa(g, e)
-      const int d = s < nkeys ? desc[s] : -1;
-      const bool swa = (d & kSwaFlag) != 0;
-      const float an = st ? a1[i] : a0[i];
-      const float ar = st ? r1[i] : r0[i];
-      const float x = cq * (swa ? p.swa_scale : p.lat_scale) * an + cr * ar;
-      kq[e] = swa ? p.pscale_swa : p.pscale_lat;
-      sv[e] = (d >= 0 && head_ok) ? x : -__builtin_inff();
-      tmax = fmaxf(tmax, sv[e]);
-      if (d >= 0) {
-        if (e < 4) m8lo |= 0xffu << (8 * e);
-        else m8hi |= 0xffu << (8 * (e - 4));
-      }
-    }
-    tmax = max_over_groups(tmax);
-    const bool grow = tmax > m_run + (float)kAttnTau;
-    if (__ballot(grow)) {
-      const float m_new = grow ? tmax : m_run;
-      const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::NDT; ++i) O[i] *= alpha;
-      m_run = m_new;
-    }
-    const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
-    float pr[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pr[e] = (sv[e] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(sv[e] - msub);
-      psum += pr[e];
-    }
-    l_run += psum;
-    // -- P operands for nope: two E4M3 terms hi + lo of p x key-scale ratio x
-    //    2^(8 - tau) (lo = the rounding residual of hi); BF16 for rope
-    float px[8], pres[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) px[e] = pr[e] * kq[e];
-    const int w0 = pack4_fp8(px[0], px[1], px[2], px[3]);
-    const int w1 = pack4_fp8(px[4], px[5], px[6], px[7]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pres[e] = px[e] - fp8_to_f32(w0, e);
-      pres[4 + e] = px[4 + e] - fp8_to_f32(w1, e);
-    }
-    const int w0l = pack4_fp8(pres[0], pres[1], pres[2], pres[3]);
-    const int w1l = pack4_fp8(pres[4], pres[5], pres[6], pres[7]);
-    const long p8 = (long)(uint32_t)w0 | ((long)(uint32_t)w1 << 32);
-    const long p8l = (long)(uint32_t)w0l | ((long)(uint32_t)w1l << 32);
-    v4i pbw;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      pbw[e] = (int)((uint32_t)f32_to_bf16_bits(pr[2 * e]) | ((uint32_t)f32_to_bf16_bits(pr[2 * e + 1]) << 16));
-    const v8bf pbf = __builtin_bit_cast(v8bf, pbw);
-
-    // -- PV: O^T[dims x heads] += X^T[dims x keys] P^T[keys x heads].  The
-    //    X^T bytes of masked keys are cleared (their LDS rows are a dummy copy)
-    {
-      const int krow = 32 * kh + kappa(g, r >> 1);
-      const uint8_t* a8 = xb + 16 * slot_of(krow) + 8 * (r & 1);
-      // transpose reads in batches of PVB issued ahead of their MFMAs
-      constexpr int PVB = 7;
-      static_assert(C::ND % PVB == 0 || C::ND < PVB, "PV batch");
-      constexpr int NB = C::ND < PVB ? 1 : C::ND / PVB;
-      constexpr int BS = C::ND < PVB ? C::ND : PVB;
-      v2i abuf[2][BS];
-#pragma unroll
-      for (int j = 0; j < BS; ++j)
-        abuf[0][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(a8 + j * kPlane));
-#pragma unroll
-      for (int bt = 0; bt < NB; ++bt) {
-        if (bt + 1 < NB) {
-#pragma unroll
-          for (int j = 0; j < BS; ++j)
-            abuf[(bt + 1) & 1][j] =
-                __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(a8 + ((bt + 1) * BS + j) * kPlane));
-        }
-#pragma unroll
-        for (int j = 0; j < BS; ++j) {
-          const int dt = bt * BS + j;
-          const v2i a = abuf[bt & 1][j];
-          const long al = (long)((uint32_t)a[0] & m8lo) | ((long)((uint32_t)a[1] & m8hi) << 32);
-          O[dt] = mfma_f8_32(al, p8, O[dt]);
-          O[dt] = mfma_f8_32(al, p8l, O[dt]);
+        for (int i = 0; i < C::PPW; ++i) {
+          const int c = wave + 4 * i;
+          if (c < C::CH) *reinterpret_cast<v4i*>(xb + c * kPlane + 16 * slot_of(lane)) = (v4i){0, 0, 0, 0};
         }
       }
-      // rope, 16-bit elements: element e of read 0 / read 1 is key kappa(g, e) / kappa(g, 4 + e)
-      const uint32_t mr0 = ((m8lo & 0xffu) ? 0xffffu : 0u) | ((m8lo & 0xff00u) ? 0xffff0000u : 0u);
-      const uint32_t mr1 = ((m8lo & 0xff0000u) ? 0xffffu : 0u) | ((m8lo & 0xff000000u) ? 0xffff0000u : 0u);
-      const uint32_t mr2 = ((m8hi & 0xffu) ? 0xffffu : 0u) | ((m8hi & 0xff00u) ? 0xffff0000u : 0u);
-      const uint32_t mr3 = ((m8hi & 0xff0000u) ? 0xffffu : 0u) | ((m8hi & 0xff000000u) ? 0xffff0000u : 0u);
-      const int krow0 = 32 * kh + kappa(g, r >> 2);
-      const int krow1 = 32 * kh + kappa(g, 4 + (r >> 2));
-      const int cpl = C::CHN + ((r >> 1) & 1);
-      const uint8_t* b0 = xb + cpl * kPlane + 16 * slot_of(krow0) + 8 * (r & 1);
-      const uint8_t* b1 = xb + cpl * kPlane + 16 * slot_of(krow1) + 8 * (r & 1);
+      lds_barrier();
+    }
+    // a tile holds only compressed entries or only window rows
+    const bool tile_swa = kv0 + it * kAttnTile >= sel_end;
+
+    // -- partial scores over this half's dims: four 16-key subtiles; the
+    //    operands of the next step are read before the MFMAs of this one
+    v4f acc[4], racc[4];
 #pragma unroll
-      for (int dt = 0; dt < C::NDR; ++dt) {
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(b0 + 2 * dt * kPlane));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(b1 + 2 * dt * kPlane));
-        v4i packed;
-        packed[0] = (int)(((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16)) & mr0);
-        packed[1] = (int)(((uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16)) & mr1);
-        packed[2] = (int)(((uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16)) & mr2);
-        packed[3] = (int)(((uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)) & mr3);
-        O[C::ND + dt] = mfma_bf16_32(__builtin_bit_cast(v8bf, packed), pbf, O[C::ND + dt]);
+    for (int st = 0; st < 4; ++st) {
+      acc[st] = (v4f){0.f, 0.f, 0.f, 0.f};
+      racc[st] = acc[st];
+    }
+    if (tile_ok) {
+      constexpr int NSTEP = HF::FB + (HF::COMB ? 1 : 0);
+      auto read_step = [&](int step, v8i (&x)[4]) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (step < HF::FB) {
+            const int c0 = 8 * (HF::FB0 + step) + 2 * g;
+            const v4i lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + qk_row[st]);
+            const v4i hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + qk_row[st]);
+            x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            const int c0 = 8 * C::NFB + 2 * (g & 1);
+            v4i lo = (v4i){0, 0, 0, 0}, hi = lo;
+            if (32 * (g & 1) < C::REM) lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + qk_row[st]);
+            if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + qk_row[st]);
+            x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        }
+      };
+      v8i x[2][4];
+      v4i y[HF::NR > 0 ? HF::NR : 1][4];
+      if (NSTEP > 0) read_step(0, x[0]);
+#pragma unroll
+      for (int rr = 0; rr < HF::NR; ++rr) {
+        const int c = C::CHN + 4 * rr + g;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          y[rr][st] = (v4i){0, 0, 0, 0};
+          if (32 * rr + 8 * g < DR) y[rr][st] = *reinterpret_cast<const v4i*>(xb + c * kPlane + qk_row[st]);
+        }
+      }
+#pragma unroll
+      for (int step = 0; step < NSTEP; ++step) {
+        if (step + 1 < NSTEP) read_step(step + 1, x[(step + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (step < HF::FB) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qhi[step], acc[st]);
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qlo[step], acc[st]);
+        } else {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qcomb, acc[st]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int rr = 0; rr < HF::NR; ++rr)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          racc[st] = mfma_bf16_32(__builtin_bit_cast(v8bf, y[rr][st]), qr[rr], racc[st]);
+    }
+
+    // -- own partial (scaled), exchanged with the other dim half of the head
+    //    tile; half 0 carries -inf for masked keys (lane keys 16 st + 4 g + i)
+    const float ks = tile_swa ? cqs : cql;
+    v4f part[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      part[st] = acc[st] * ks;
+      if (DH == 1) part[st] += racc[st] * cr;
+    }
+    if (DH == 0 && !full) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint32_t vw = st < 2 ? (uint32_t)vmask : (uint32_t)(vmask >> 32);
+        const uint32_t bits = vw >> (16 * (st & 1) + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((bits >> i) & 1u)) part[st][i] = -__builtin_inff();
       }
     }
-  }
-  __syncthreads();   // every wave is done with the tile buffers
+#pragma unroll
+    for (int st = 0; st < 4; ++st) sx_own[st * 64] = part[st];
+    if (refill) issue_tile(it + 2, nbuf, 1);
+    lds_barrier();
+    v4f oth[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) oth[st] = sx_oth[st * 64];
+    __builtin_amdgcn_sched_barrier(0);
 
-  // ---- merge the two key halves (kh) of each head tile through LDS
-  const float l_tot = sum_over_groups(l_run);
-  float* ex = reinterpret_cast<float*>(&xs[0][0]);                   // [4][HALF][64][4]
-  float* stt = ex + 4 * C::HALF * 64 * 4;                              // [4][64][2]
-  if (kh == 0) {
+    if (tile_ok) {
+      // -- online softmax (lane: head h, keys 16 st + 4 g + i)
+      float sv[16];
+      float tmax = -__builtin_inff();
 #pragma unroll
-    for (int j = 0; j < C::HALF; ++j)
-      *reinterpret_cast<v4f*>(ex + ((wave * C::HALF + j) * 64 + lane) * 4) = O[C::HALF + j];
-  } else {
+      for (int st = 0; st < 4; ++st) {
+        const v4f tot = DH == 0 ? part[st] + oth[st] : oth[st] + part[st];
 #pragma unroll
-    for (int j = 0; j < C::HALF; ++j)
-      *reinterpret_cast<v4f*>(ex + ((wave * C::HALF + j) * 64 + lane) * 4) = O[j];
+        for (int i = 0; i < 4; ++i) {
+          sv[4 * st + i] = tot[i];
+          tmax = fmaxf(tmax, tot[i]);
+        }
+      }
+      tmax = max_over_groups(tmax);
+      const bool grow = tmax > m_run + (float)kAttnTau;
+      if (__ballot(grow)) {
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
+        m_run = m_new;
+      }
+      const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+      float pr[16];
+      float psum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pr[e] = __builtin_amdgcn_exp2f(sv[e] - msub);   // exp2(-inf) = 0 for masked keys
+        psum += pr[e];
+      }
+      l_run += psum;
+
+      // -- P operand for nope: bytes [hi of the lane's 16 keys | lo of them]
+      //    of p x key-scale ratio x 2^(8 - tau); lo = the rounding residual
+      const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
+      v8i pb;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float x0 = pr[4 * st] * kq, x1 = pr[4 * st + 1] * kq;
+        const float x2 = pr[4 * st + 2] * kq, x3 = pr[4 * st + 3] * kq;
+        const int w = pack4_fp8(x0, x1, x2, x3);
+        const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const v2f b23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        pb[st] = w;
+        pb[4 + st] = pack4_fp8(x0 - b01[0], x1 - b01[1], x2 - b23[0], x3 - b23[1]);
+      }
+
+      // -- PV: O^T[dims x heads] += X^T[dims x K] P^T[K x heads]; A = the
+      //    two 8-key transpose reads, used for the hi and the lo half of K.
+      //    Reads of the next batch go out before the MFMAs of this one.
+      {
+        constexpr int PB = 4;   // dim tiles per batch
+        constexpr int NB = (HF::NPT + PB - 1) / PB;
+        v2i ra[2][PB], rb[2][PB];
+        auto read_batch = [&](int bt, v2i (&a)[PB], v2i (&b)[PB]) {
+#pragma unroll
+          for (int j = 0; j < PB; ++j) {
+            const int dt = bt * PB + j;
+            if (dt < HF::NPT) {
+              const uint8_t* pl = xb + (HF::PT0 + dt) * kPlane;
+              a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(pl + pv0));
+              b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(pl + pv1));
+            }
+          }
+        };
+        if (NB > 0) read_batch(0, ra[0], rb[0]);
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt) {
+          if (bt + 1 < NB) read_batch(bt + 1, ra[(bt + 1) & 1], rb[(bt + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < PB; ++j) {
+            const int dt = bt * PB + j;
+            if (dt < HF::NPT) {
+              const v2i a0 = ra[bt & 1][j], a1 = rb[bt & 1][j];
+              const v8i a = (v8i){a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};
+              O[dt] = mfma_f8_128(a, pb, O[dt]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (HF::NRT > 0) {
+        // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7)
+        v4i pbf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pbf[u][e] = (int)pack2_bf16(pr[8 * u + 2 * e], pr[8 * u + 2 * e + 1]);
+        v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
+#pragma unroll
+        for (int j = 0; j < HF::NRT; ++j) {
+          const uint8_t* pl = xb + 2 * j * kPlane;
+          const v2i l0 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp0)));
+          const v2i h0 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp1)));
+          const v2i l1 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp2)));
+          const v2i h1 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp3)));
+          ya[j][0] = (v4i){l0[0], l0[1], h0[0], h0[1]};
+          ya[j][1] = (v4i){l1[0], l1[1], h1[0], h1[1]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < HF::NRT; ++j)
+            O[HF::NPT + j] = mfma_bf16_32(__builtin_bit_cast(v8bf, ya[j][u]), __builtin_bit_cast(v8bf, pbf[u]),
+                                          O[HF::NPT + j]);
+      }
+    }
+    if (refill) issue_tile(it + 2, nbuf, 2);
   }
-  stt[(wave * 64 + lane) * 2 + 0] = m_run;
-  stt[(wave * 64 + lane) * 2 + 1] = l_tot;
-  __syncthreads();
   if (!tile_ok) return;
-  const int partner = wave ^ 2;
-  const float pm = stt[(partner * 64 + lane) * 2 + 0];
-  const float pl = stt[(partner * 64 + lane) * 2 + 1];
-  const float M = fmaxf(m_run, pm);
-  const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
-  const float a_self = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - Ms);
-  const float a_oth = (pm == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(pm - Ms);
-  const float L = l_tot * a_self + pl * a_oth;
+
+  // ---- output of this half's dims (the softmax state is the same in both halves)
+  const float L = sum_over_groups(l_run);
+  const float M = m_run;
   const bool final_out = p.n_splits == 1;
   const float invL = (final_out && L > 0.0f) ? 1.0f / L : 0.0f;
+  if (head_ok) {
+#pragma unroll
+    for (int j = 0; j < HF::NO; ++j) {
+      const bool nope = j < HF::NPT;
+      const float unit = nope ? p.nope_unit : 1.0f;
+      const int dim = nope ? 16 * (HF::PT0 + j) + 4 * g : DN + 16 * (j - HF::NPT) + 4 * g;
+      const v4f v = O[j] * unit;
+      if (final_out) {
+        const v2i pk = (v2i){(int)pack2_bf16(v[0] * invL, v[1] * invL), (int)pack2_bf16(v[2] * invL, v[3] * invL)};
+        *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + dim) = pk;
+      } else {
+        *reinterpret_cast<v4f*>(p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + 2) + dim) = v;
+      }
+    }
+    if (DH == 0 && g == 0) {
+      if (final_out) {
+        if (p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
+      } else {
+        float* dst = p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + 2) + D;
+        dst[0] = M;
+        dst[1] = L;
+      }
+    }
+  }
+}
 
-  auto finish = [&](int dt, const v4f& own) {
-    const v4f oth = *reinterpret_cast<const v4f*>(ex + ((partner * C::HALF + (dt - kh * C::HALF)) * 64 + lane) * 4);
-    const bool nope = dt < C::ND;
-    const float unit = nope ? p.nope_unit : 1.0f;
-    const int dim = nope ? 16 * dt + 4 * g : DN + 16 * (dt - C::ND) + 4 * g;
-    v4f v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (own[i] * a_self + oth[i] * a_oth) * unit;
-    if (!head_ok) return;
-    if (final_out) {
-      const uint32_t b0 = f32_to_bf16_bits(v[0] * invL), b1 = f32_to_bf16_bits(v[1] * invL);
-      const uint32_t b2 = f32_to_bf16_bits(v[2] * invL), b3 = f32_to_bf16_bits(v[3] * invL);
-      v2i pk = (v2i){(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
-      *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + dim) = pk;
-    } else {
-      float* dst = p.part + (((size_t)split * p.T + t) * p.H + h) * (D + 2) + dim;
-      *reinterpret_cast<v4f*>(dst) = v;
-    }
-  };
-  if (kh == 0) {
-#pragma unroll
-    for (int j = 0; j < C::HALF; ++j) finish(j, O[j]);
+template <int DN, int DR>
+__global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
+  using C = Cfg<DN, DR>;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf * C::TILE_BYTES];
+  __shared__ int32_t desc[kAttnMaxSlots];
+  __shared__ v4f sx[4 * 4 * 64];   // partial score tiles, [wave][subtile][lane]
+
+  // ---- which (query, head group, split).  Workgroups go to the 8 XCDs
+  // round-robin by id.  With 8 or more queries, queries are spread over the
+  // XCDs and all workgroups of one query share an XCD (and its L2, which then
+  // serves the head groups' repeated reads of the same rows); with fewer,
+  // a query's workgroups are spread over all XCDs instead.
+  const int nb = p.n_hg * p.n_splits;
+  const int bid = blockIdx.x;
+  Block bk;
+  int jb;
+  if (p.T >= 8) {
+    const int local = bid >> 3;
+    bk.t = (local / nb) * 8 + (bid & 7);
+    jb = local % nb;
   } else {
-#pragma unroll
-    for (int j = 0; j < C::HALF; ++j) finish(C::HALF + j, O[C::HALF + j]);
+    bk.t = bid / nb;
+    jb = bid - bk.t * nb;
   }
-  if (head_ok && kh == 0 && g == 0) {
-    if (final_out) {
-      if (p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
-    } else {
-      float* dst = p.part + (((size_t)split * p.T + t) * p.H + h) * (D + 2) + D;
-      dst[0] = M;
-      dst[1] = L;
-    }
+  if (bk.t >= p.T) return;
+  bk.hg = jb / p.n_splits;
+  bk.split = jb - bk.hg * p.n_splits;
+  const bool prefill = p.prefill_seq >= 0;
+  bk.seq = prefill ? p.prefill_seq : bk.t;
+  bk.pos = p.q_pos[bk.t];
+  bk.nc = p.n_comp[bk.seq];
+  // with a top-k list the slot count needs nothing loaded, so the
+  // descriptor loads need not wait for the position
+  if (p.topk) {
+    bk.n_sel = p.k;
+  } else {
+    bk.n_sel = bk.pos >= 0 ? max(0, min(bk.pos / p.ratio_m, bk.nc)) : 0;
   }
+  // the selected slots are padded to whole tiles, so that no tile mixes
+  // compressed entries and window rows
+  bk.sel_end = (bk.n_sel + kAttnTile - 1) & ~(kAttnTile - 1);
+  const int n_slots = bk.sel_end + p.W;
+  bk.kv0 = bk.split * p.per_split;
+  if (bk.split > 0 && bk.kv0 >= n_slots) return;   // empty split: the merge skips it
+  bk.nkeys = max(0, min(n_slots, bk.kv0 + p.per_split) - bk.kv0);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < 4);
+  if (wave >= 2)
+    attn_wave<DN, DR, 1>(p, bk, xs, desc, sx, wave);
+  else
+    attn_wave<DN, DR, 0>(p, bk, xs, desc, sx, wave);
 }
 
 // Combines the per-split partial states (unnormalised O, running max in log2
@@ -587,7 +689,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int seq = prefill ? p.prefill_seq : t;
   const int pos = p.q_pos[t];
   const int nv = pos >= 0 ? max(0, min(pos / p.ratio_m, p.n_comp[seq])) : 0;
-  const int n_slots = (p.topk ? p.k : nv) + p.W;
+  const int n_slots = (((p.topk ? p.k : nv) + kAttnTile - 1) & ~(kAttnTile - 1)) + p.W;
   const int used = max(1, min(p.n_splits, (n_slots + p.per_split - 1) / p.per_split));
   float M = -__builtin_inff();
   for (int s = 0; s < used; ++s) M = fmaxf(M, p.part[(((size_t)s * p.T + t) * p.H + h) * (D + 2) + D]);
@@ -603,10 +705,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     acc += v * a;
   }
   const float invL = L > 0.0f ? 1.0f / L : 0.0f;
-  const uint32_t b0 = f32_to_bf16_bits(acc[0] * invL), b1 = f32_to_bf16_bits(acc[1] * invL);
-  const uint32_t b2 = f32_to_bf16_bits(acc[2] * invL), b3 = f32_to_bf16_bits(acc[3] * invL);
   *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + d0) =
-      (v2i){(int)(b0 | (b1 << 16)), (int)(b2 | (b3 << 16))};
+      (v2i){(int)pack2_bf16(acc[0] * invL, acc[1] * invL), (int)pack2_bf16(acc[2] * invL, acc[3] * invL)};
   if (d0 == 0 && p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
 }
 

@@ -61,7 +61,8 @@ size_t partial_bytes(int64_t T, int64_t H, int D, int splits) {
 bool plan_attn(int64_t T, int32_t H, int D, int64_t max_slots, size_t ws_avail, bool limit_ws, AttnPlan* out) {
   AttnPlan pl;
   pl.n_hg = (int)ceil_div(H, 32);
-  const int64_t slots = std::max<int64_t>(1, max_slots);
+  // the kernel pads the selected slots to whole tiles (at most kAttnTile - 1 more)
+  const int64_t slots = std::max<int64_t>(1, max_slots + kAttnTile - 1);
   const int64_t min_splits = ceil_div(slots, kAttnMaxSlots);
   const int64_t base = std::max<int64_t>(1, T * pl.n_hg);
   int64_t splits = std::max<int64_t>(min_splits, ceil_div(kTargetBlocks, base));
@@ -207,6 +208,16 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
   p.pscale_lat = p.lat_scale / smax * pmul;
   p.pscale_swa = p.swa_scale / smax * pmul;
   p.nope_unit = smax / pmul;
+  // division by the page size as a multiply-shift: with l = ceil(log2 d),
+  // M = ceil(2^(32 + l) / d) has M d - 2^(32 + l) < d <= 2^l, so
+  // floor(n M / 2^(32 + l)) == floor(n / d) for every n < 2^31
+  {
+    int l = 0;
+    while ((1LL << l) < p.page_size) ++l;
+    const unsigned __int128 num = (unsigned __int128)1 << (32 + l);
+    p.ps_magic = (uint64_t)((num + (unsigned)p.page_size - 1) / (unsigned)p.page_size);
+    p.ps_shift = 32 + l;
+  }
   AttnPlan pl;
   const size_t avail = (workspace && aligned16(workspace)) ? workspace_bytes : 0;
   if (!plan_attn(p.T, p.H, p.D_nope + p.D_rope, max_slots, avail, true, &pl)) return CSA_ERR_WORKSPACE;

@@ -68,13 +68,12 @@ __device__ __forceinline__ float max_over_groups(float x) {
 }
 
 // ---- number formats ------------------------------------------------------
-// Round-to-nearest-even FP32 -> BF16 bits, branch-free; NaN stays a quiet
-// NaN, infinities stay infinities.
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const bool nan = (u & 0x7fffffffu) > 0x7f800000u;
-  return (uint16_t)(nan ? ((u >> 16) | 0x40u) : rounded);
+// Two floats -> two BF16 values (round to nearest even) packed low, high in
+// a 32-bit word: one v_cvt_pk_bf16_f32 on gfx950.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 

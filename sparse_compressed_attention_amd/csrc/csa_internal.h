@@ -64,6 +64,9 @@ struct AttnParams {
   // per key source (key scale / max scale * 2^(8 - tau)); value unit of the
   // FP8 accumulator (max scale / 2^(8 - tau))
   float sm_log2, pscale_lat, pscale_swa, nope_unit;
+  // entry / page_size == (entry * ps_magic) >> ps_shift for 0 <= entry < 2^31
+  uint64_t ps_magic;
+  int ps_shift;
   int num_pages, page_size, max_pages, ratio_m;
   int k, W;
   int prefill_seq;         // -1: decode (query t belongs to sequence t)
