@@ -29,11 +29,13 @@
 //    -> row) are resolved once into LDS; each 64-key tile is copied from HBM
 //    straight into LDS with global_load_lds_dwordx4 (no register staging),
 //    three tiles in flight (ring of 3 buffers, prefetch distance 2).  The
-//    tile is stored as "planes": plane c holds the c-th 16-byte chunk of all
-//    64 rows, so one DMA instruction writes one whole plane and every lane
-//    keeps one row (key) for all of its DMAs.  Rows 16..31 and 48..63 are
-//    XOR-swizzled by 4 slots against LDS bank conflicts of the transpose
-//    reads.  Rows of masked keys (padding, invalid entries, the ragged tail)
+//    tile is a grid of 256-byte blocks, each holding one 16-byte chunk of 16
+//    keys; one DMA instruction fills four blocks (16 keys x 64 contiguous
+//    bytes of their rows), so it touches 16 cache lines instead of 64, and
+//    every lane keeps one key for all of its DMAs.  Inside a block the key
+//    rows are XOR-ed with 8 on alternate blocks, which keeps the QK reads and
+//    both transpose reads free of LDS bank conflicts.  Rows of masked keys
+//    (padding, invalid entries, the ragged tail)
 //    are cleared in LDS once their DMA has landed, so no operand needs a
 //    per-key mask.  The cache's FP8/BF16 bytes go to the MFMA unchanged;
 //  * QK: S^T (keys x heads) = X . Q^T on v_mfma 16x16x128 FP8, with q split
@@ -59,7 +61,6 @@ namespace {
 
 constexpr int kSwaFlag = 1 << 30;
 constexpr int kNBuf = 3;
-constexpr int kPlane = kAttnTile * 16;   // bytes per plane (64 rows x 16 B)
 
 template <int DN, int DR>
 struct Cfg {
@@ -68,15 +69,14 @@ struct Cfg {
   static constexpr int NBLK = NFB + (REM > 0 ? 1 : 0);
   static constexpr int B0 = (NBLK + 1) / 2;                  // nope blocks of dim half 0
   static constexpr int N0 = DN < 128 * B0 ? DN : 128 * B0;   // nope dims of dim half 0
-  static constexpr int CHN = DN / 16;                        // nope planes
-  static constexpr int CHR = DR / 8;                         // rope planes
-  static constexpr int CH = CHN + CHR;
-  static constexpr int PPW = (CH + 3) / 4;                   // planes per wave (max)
-  static constexpr int PMIN = CH / 4;                        // planes per wave (min)
-  static constexpr int TILE_BYTES = CH * kPlane;
+  static constexpr int CHN = DN / 16;                        // 16-byte nope chunks of a row
+  static constexpr int CHR = DR / 8;                         // 16-byte rope chunks of a row
+  static constexpr int CHNP = (CHN + 3) & ~3;                // padded to whole quads
+  static constexpr int CHRP = (CHR + 3) & ~3;
+  static constexpr int NQ = (CHNP + CHRP) / 4;               // quads = DMAs per wave per tile
+  static constexpr int TILE_BYTES = NQ * 4 * 1024;
   static_assert(DN % 16 == 0 && DR % 16 == 0, "dims must be multiples of 16");
   static_assert(REM <= 64, "remainder block must fit one combined hi|lo MFMA");
-  static_assert(PMIN >= 1, "every wave issues at least one plane per tile");
 };
 
 // What dim half DH of a head tile owns.
@@ -98,8 +98,22 @@ struct Half {
 // key (0..31) held by byte e (0..7) of a lane in 16-lane group g: the keys
 // of the two 16-key subtiles that the QK output layout puts in that lane.
 __device__ __forceinline__ int kappa(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
-// LDS slot of key k inside a plane (an involution).
-__device__ __forceinline__ int slot_of(int k) { return k ^ (((k >> 4) & 1) << 2); }
+// Byte offset of 16-byte chunk c of tile key k.  Block (q, rg, cc) =
+// ((c / 4) * 4 + k / 16) * 4 + c % 4 holds chunk c of keys [16 rg, 16 rg + 16);
+// inside it key row k % 16 is XOR-ed with 8 when (k / 16 + c) is odd.  With
+// q = c / 4, the four blocks (q, rg, 0..3) are one contiguous KB: the target
+// of one DMA instruction.
+__device__ __forceinline__ int chunk_off(int k, int c) {
+  const int rg = k >> 4;
+  return ((((c >> 2) << 2) + rg) * 4 + (c & 3)) * 256 + 16 * ((k & 15) ^ (((rg ^ c) & 1) << 3));
+}
+// chunk_off(k, c) - chunk_base(c) for keys k = 16 st + row: the part that
+// depends on the key (c enters only through its parity)
+__device__ __forceinline__ int chunk_base(int c) { return (((c >> 2) << 4) + (c & 3)) * 256; }
+__device__ __forceinline__ int key_part(int k, int parity) {
+  const int rg = k >> 4;
+  return rg * 1024 + 16 * ((k & 15) ^ (((rg ^ parity) & 1) << 3));
+}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -246,14 +260,16 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 
   __syncthreads();   // descriptors visible
 
-  // ---- tile DMA: lane -> the key whose plane slot is `lane`, planes
-  // c = wave + 4 i.  Masked keys copy a dummy row (row 0) so that every wave
-  // issues the same number of DMAs per tile; those rows are cleared in LDS
-  // before use.
-  const int dkey = slot_of(lane);
-  constexpr int kParts = 3;                          // a tile's DMAs go out in three parts
-  constexpr int kPerPart = (C::PPW + kParts - 1) / kParts;
-  auto issue_tile = [&](int tile, int buf, int part) {
+  // ---- tile DMA: wave w fills the quads of keys [16 w, 16 w + 16); lane l
+  // copies 16 bytes of chunk 4 q + l / 16 of key dkey into LDS byte
+  // (q * 4 + w) * 1024 + 16 l.  Masked keys copy a dummy row (row 0) so that
+  // every wave issues the same number of DMAs per tile; those rows are
+  // cleared in LDS before use.
+  const int dcc = lane >> 4;
+  const int dkey = 16 * wave + ((lane & 15) ^ (((wave ^ dcc) & 1) << 3));
+  const uint8_t* tsrc_n = p.lat_nope;   // this lane's row of the tile being issued
+  const uint8_t* tsrc_r = reinterpret_cast<const uint8_t*>(p.lat_rope);
+  auto prep_tile = [&](int tile) {
     const int s = tile * kAttnTile + dkey;
     const int d = s < nkeys ? desc[s] : -1;
     const uint8_t* nsrc = p.lat_nope;
@@ -268,20 +284,38 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         rsrc = reinterpret_cast<const uint8_t*>(p.lat_rope + row * DR);
       }
     }
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(CSA_LDS uint8_t*)(xs0 + buf * C::TILE_BYTES);
+    tsrc_n = nsrc;
+    tsrc_r = rsrc;
+  };
+  constexpr int kParts = 3;                          // a tile's DMAs go out in three parts
+  constexpr int kPerPart = (C::NQ + kParts - 1) / kParts;
+  auto issue_quads = [&](int buf, int part) {
+    const uint32_t lds_base =
+        (uint32_t)(uintptr_t)(CSA_LDS uint8_t*)(xs0 + buf * C::TILE_BYTES) + (uint32_t)wave * 1024u;
 #pragma unroll
-    for (int i = 0; i < C::PPW; ++i) {
-      const int c = wave + 4 * i;
-      if (c < C::CH && (part < 0 || i / kPerPart == part)) {
-        const uint8_t* src = (c < C::CHN) ? nsrc + 16 * c : rsrc + 16 * (c - C::CHN);
-        dma16(src, lds_base + c * kPlane);
+    for (int q = 0; q < C::NQ; ++q) {
+      if (part >= 0 && q / kPerPart != part) continue;
+      const int c = 4 * q + dcc;
+      const uint8_t* src;
+      if (4 * q < C::CHNP) {
+        src = (C::CHN == C::CHNP || c < C::CHN) ? tsrc_n + 16 * c : tsrc_n;
+      } else {
+        const int cr = c - C::CHNP;
+        src = (C::CHR == C::CHRP || cr < C::CHR) ? tsrc_r + 16 * cr : tsrc_r;
       }
+      dma16(src, lds_base + q * 4096);
     }
   };
 
   const int n_tiles = (nkeys + kAttnTile - 1) / kAttnTile;
-  if (n_tiles > 0) issue_tile(0, 0, -1);
-  if (n_tiles > 1) issue_tile(1, 1, -1);
+  if (n_tiles > 0) {
+    prep_tile(0);
+    issue_quads(0, -1);
+  }
+  if (n_tiles > 1) {
+    prep_tile(1);
+    issue_quads(1, -1);
+  }
 
   // ---- query operands: q split into two E4M3 terms hi + lo with a shared
   // power-of-two per-head scale over this half's nope dims
@@ -340,17 +374,27 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 #pragma unroll
   for (int i = 0; i < HF::NO; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // loop-invariant LDS byte offsets
-  int qk_row[4];                                      // QK: key 16 st + r
+  // loop-invariant per-lane parts of the LDS offsets
+  int qk_off[4][2];                                          // key 16 st + r, chunk parity
 #pragma unroll
-  for (int st = 0; st < 4; ++st) qk_row[st] = 16 * slot_of(16 * st + r);
-  const int pv0 = 16 * slot_of(kappa(g, r >> 1)) + 8 * (r & 1);        // tr8 rows, keys 0..31
-  const int pv1 = 16 * slot_of(32 + kappa(g, r >> 1)) + 8 * (r & 1);   // keys 32..63
-  const int rp_pl = C::CHN + ((r >> 1) & 1);
-  const int rp0 = rp_pl * kPlane + 16 * slot_of(kappa(g, r >> 2)) + 8 * (r & 1);
-  const int rp1 = rp_pl * kPlane + 16 * slot_of(kappa(g, 4 + (r >> 2))) + 8 * (r & 1);
-  const int rp2 = rp_pl * kPlane + 16 * slot_of(32 + kappa(g, r >> 2)) + 8 * (r & 1);
-  const int rp3 = rp_pl * kPlane + 16 * slot_of(32 + kappa(g, 4 + (r >> 2))) + 8 * (r & 1);
+  for (int st = 0; st < 4; ++st) {
+    qk_off[st][0] = key_part(16 * st + r, 0);
+    qk_off[st][1] = key_part(16 * st + r, 1);
+  }
+  const int qk_g = ((g >> 1) * 16 + 2 * (g & 1)) * 256;      // chunk_base(2 g) for the full blocks
+  int pv_off[2][2];                                          // tr8 rows: keys 32 u + kappa(g, r / 2), parity
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    pv_off[u][0] = key_part(32 * u + kappa(g, r >> 1), 0) + 8 * (r & 1);
+    pv_off[u][1] = key_part(32 * u + kappa(g, r >> 1), 1) + 8 * (r & 1);
+  }
+  const int rb_ = (r >> 1) & 1;                              // rope tr16: chunk parity of this lane
+  int rp_off[2][2];                                          // [u][lo/hi key group]
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    rp_off[u][0] = rb_ * 256 + key_part(32 * u + kappa(g, r >> 2), rb_) + 8 * (r & 1);
+    rp_off[u][1] = rb_ * 256 + key_part(32 * u + kappa(g, 4 + (r >> 2)), rb_) + 8 * (r & 1);
+  }
   v4f* sx_own = sx + (size_t)wave * 4 * 64 + lane;
   const v4f* sx_oth = sx + (size_t)(wave ^ 2) * 4 * 64 + lane;
 
@@ -359,12 +403,15 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     // tile `it` landed in LDS (this wave's DMAs), then everyone's (barrier);
     // the barrier also retires every wave's reads of the buffer reused next
     asm volatile("" ::: "memory");
-    if (it + 1 < n_tiles) wait_vmcnt<C::PMIN>(); else wait_vmcnt<0>();
+    if (it + 1 < n_tiles) wait_vmcnt<C::NQ>(); else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const bool refill = it + 2 < n_tiles;
     const int nbuf = buf == 0 ? 2 : buf - 1;
-    if (refill) issue_tile(it + 2, nbuf, 0);
+    if (refill) {
+      prep_tile(it + 2);
+      issue_quads(nbuf, 0);
+    }
     uint8_t* xb = xs0 + buf * C::TILE_BYTES;
 
     // -- valid keys of the tile (the same in every wave): bit k = key k.
@@ -374,12 +421,10 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     const uint64_t vmask = __ballot(dk >= 0);
     const bool full = vmask == ~0ull;
     if (!full) {
-      if (dk < 0) {
+      if (!((vmask >> dkey) & 1ull)) {
 #pragma unroll
-        for (int i = 0; i < C::PPW; ++i) {
-          const int c = wave + 4 * i;
-          if (c < C::CH) *reinterpret_cast<v4i*>(xb + c * kPlane + 16 * slot_of(lane)) = (v4i){0, 0, 0, 0};
-        }
+        for (int q = 0; q < C::NQ; ++q)
+          *reinterpret_cast<v4i*>(xb + (q * 4 + wave) * 1024 + 16 * lane) = (v4i){0, 0, 0, 0};
       }
       lds_barrier();
     }
@@ -400,15 +445,17 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           if (step < HF::FB) {
-            const int c0 = 8 * (HF::FB0 + step) + 2 * g;
-            const v4i lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + qk_row[st]);
-            const v4i hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + qk_row[st]);
+            // chunks 8 (FB0 + step) + 2 g and + 1 (even, odd)
+            const uint8_t* base = xb + (HF::FB0 + step) * 8192 + qk_g;
+            const v4i lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
+            const v4i hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
             x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           } else {
-            const int c0 = 8 * C::NFB + 2 * (g & 1);
+            // chunks 8 NFB + 2 (g & 1) and + 1
+            const uint8_t* base = xb + C::NFB * 8192 + 512 * (g & 1);
             v4i lo = (v4i){0, 0, 0, 0}, hi = lo;
-            if (32 * (g & 1) < C::REM) lo = *reinterpret_cast<const v4i*>(xb + c0 * kPlane + qk_row[st]);
-            if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(xb + (c0 + 1) * kPlane + qk_row[st]);
+            if (32 * (g & 1) < C::REM) lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
+            if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
             x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
         }
@@ -418,11 +465,12 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
       if (NSTEP > 0) read_step(0, x[0]);
 #pragma unroll
       for (int rr = 0; rr < HF::NR; ++rr) {
-        const int c = C::CHN + 4 * rr + g;
+        // rope chunk CHNP + 4 rr + g (parity g & 1)
+        const uint8_t* base = xb + ((C::CHNP / 4 + rr) * 16 + g) * 256;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           y[rr][st] = (v4i){0, 0, 0, 0};
-          if (32 * rr + 8 * g < DR) y[rr][st] = *reinterpret_cast<const v4i*>(xb + c * kPlane + qk_row[st]);
+          if (32 * rr + 8 * g < DR) y[rr][st] = *reinterpret_cast<const v4i*>(base + qk_off[st][g & 1]);
         }
       }
 #pragma unroll
@@ -448,13 +496,20 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     }
 
     // -- own partial (scaled), exchanged with the other dim half of the head
-    //    tile; half 0 carries -inf for masked keys (lane keys 16 st + 4 g + i)
+    //    tile.  Half 0 also subtracts the running max (so the sum S' is the
+    //    exp2 argument) and carries -inf for masked keys (lane keys
+    //    16 st + 4 g + i).
+    const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
     const float ks = tile_swa ? cqs : cql;
     v4f part[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      part[st] = acc[st] * ks;
-      if (DH == 1) part[st] += racc[st] * cr;
+      if (DH == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[st][i] = __builtin_fmaf(acc[st][i], ks, -msub);
+      } else {
+        part[st] = acc[st] * ks + racc[st] * cr;
+      }
     }
     if (DH == 0 && !full) {
 #pragma unroll
@@ -468,7 +523,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st) sx_own[st * 64] = part[st];
-    if (refill) issue_tile(it + 2, nbuf, 1);
+    if (refill) issue_quads(nbuf, 1);
     lds_barrier();
     v4f oth[4];
 #pragma unroll
@@ -476,7 +531,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     __builtin_amdgcn_sched_barrier(0);
 
     if (tile_ok) {
-      // -- online softmax (lane: head h, keys 16 st + 4 g + i)
+      // -- online softmax (lane: head h, keys 16 st + 4 g + i); sv = S - msub
       float sv[16];
       float tmax = -__builtin_inff();
 #pragma unroll
@@ -489,22 +544,31 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         }
       }
       tmax = max_over_groups(tmax);
-      const bool grow = tmax > m_run + (float)kAttnTau;
-      if (__ballot(grow)) {
-        const float m_new = grow ? tmax : m_run;
-        const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
-        m_run = m_new;
-      }
-      const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+      const bool m_inf = m_run == -__builtin_inff();
+      const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
       float pr[16];
       float psum = 0.0f;
+      if (__ballot(grow)) {
+        // raise the running max to the tile max on the lanes that grew
+        const float delta = grow ? tmax : 0.0f;
+        const float alpha = grow ? (m_inf ? 0.0f : __builtin_amdgcn_exp2f(-tmax)) : 1.0f;
+        if (grow) m_run = msub + tmax;
+        l_run *= alpha;
+        if (it > 0) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(sv[e] - msub);   // exp2(-inf) = 0 for masked keys
-        psum += pr[e];
+          for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          pr[e] = __builtin_amdgcn_exp2f(sv[e] - delta);
+          psum += pr[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          pr[e] = __builtin_amdgcn_exp2f(sv[e]);   // exp2(-inf) = 0 for masked keys
+          psum += pr[e];
+        }
       }
       l_run += psum;
 
@@ -535,9 +599,10 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
           for (int j = 0; j < PB; ++j) {
             const int dt = bt * PB + j;
             if (dt < HF::NPT) {
-              const uint8_t* pl = xb + (HF::PT0 + dt) * kPlane;
-              a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(pl + pv0));
-              b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(pl + pv1));
+              const int c = HF::PT0 + dt;
+              const uint8_t* cb = xb + chunk_base(c);
+              a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[0][c & 1]));
+              b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[1][c & 1]));
             }
           }
         };
@@ -559,7 +624,8 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         }
       }
       if (HF::NRT > 0) {
-        // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7)
+        // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7); rope dim tile
+        // j = chunks CHNP + 2 j (+1)
         v4i pbf[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -568,13 +634,13 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
 #pragma unroll
         for (int j = 0; j < HF::NRT; ++j) {
-          const uint8_t* pl = xb + 2 * j * kPlane;
-          const v2i l0 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp0)));
-          const v2i h0 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp1)));
-          const v2i l1 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp2)));
-          const v2i h1 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(pl + rp3)));
-          ya[j][0] = (v4i){l0[0], l0[1], h0[0], h0[1]};
-          ya[j][1] = (v4i){l1[0], l1[1], h1[0], h1[1]};
+          const uint8_t* cb = xb + ((C::CHNP / 4 + (j >> 1)) * 16 + 2 * (j & 1)) * 256;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const v2i lo = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][0])));
+            const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][1])));
+            ya[j][u] = (v4i){lo[0], lo[1], hi[0], hi[1]};
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -585,7 +651,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
                                           O[HF::NPT + j]);
       }
     }
-    if (refill) issue_tile(it + 2, nbuf, 2);
+    if (refill) issue_quads(nbuf, 2);
   }
   if (!tile_ok) return;
 
