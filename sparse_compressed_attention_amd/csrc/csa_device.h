@@ -4,6 +4,9 @@
 //  * v_mfma_f32_16x16x128_f8f6f4 (FP8 E4M3 A and B, unit scales):
 //      A[m = r][k = 32g .. 32g+31] (32 bytes per lane), B[k = 32g..][n = r],
 //      C[m = 4g + i][n = r] for i = 0..3.
+//  * v_mfma_f32_32x32x64_f8f6f4 (FP8 A and B, unit scales):
+//      A[m = l % 32][k = 32 (l / 32) .. + 31], B[k = 32 (l / 32) ..][n = l % 32],
+//      C[m = (i / 4) 8 + (l / 32) 4 + i % 4][n = l % 32] for i = 0..15.
 //  * v_mfma_f32_16x16x32_fp8_fp8 and v_mfma_f32_16x16x32_bf16:
 //      A[m = r][k = 8g .. 8g+7], B[k = 8g..][n = r], C as above.
 //  Only the pairing matters for correctness: byte/element e of lane l's A
@@ -27,6 +30,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 #define CSA_LDS __attribute__((address_space(3)))
@@ -40,6 +44,9 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ v4f mfma_f8_128(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+__device__ __forceinline__ v16f mfma_f8_32x32(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 __device__ __forceinline__ v4f mfma_f8_32(long a, long b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
@@ -48,8 +55,11 @@ __device__ __forceinline__ v4f mfma_bf16_32(const v8bf& a, const v8bf& b, const 
 }
 
 // ---- cross-lane reductions over the four 16-lane groups ------------------
-// v_permlane32_swap(x, x) leaves lane l holding (x[l & 31], x[(l & 31) + 32]);
-// v_permlane16_swap(x, x) does the same for rows of 16 within each half.
+// v_permlane32_swap(a, b) returns (a, b) with the upper half's a swapped
+// for the lower half's b: lanes 0..31 get (a, a[l + 32]), lanes 32..63 get
+// (b[l - 32], b).  So swap(x, x) leaves lane l holding (x[l & 31],
+// x[(l & 31) + 32]).  v_permlane16_swap does the same for rows of 16 within
+// each half (partner lane l ^ 16).
 __device__ __forceinline__ float sum_over_groups(float x) {
   int xi = __float_as_int(x);
   auto a = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);

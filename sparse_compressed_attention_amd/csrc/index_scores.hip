@@ -37,30 +37,52 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r = lane & 15;
+  const bool dim_ok = 32 * g < p.D_I;
 
+  // ---- first round trip: the query operand and head weights (they depend
+  // only on t), the position and the page ids, all issued before anything
+  // is waited for.  Query operand: 4 tiles of 16 index heads; lane holds
+  // head 16 ht + r, dims [32 g, 32 g + 32).  Weights of output rows
+  // (heads 16 ht + 4 g + i), read as one 16-byte load per tile.
+  v8i qa[4];
+  v4f wv[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = 16 * ht + r;
+    qa[ht] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    if (h < p.H_I && dim_ok) {
+      const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
+      const v4i lo = ld16(src), hi = ld16(src + 16);
+      qa[ht] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    const int h0 = 16 * ht + 4 * g;
+    if (h0 + 3 < p.H_I && (p.H_I & 3) == 0 && ((uintptr_t)p.w & 15) == 0) {
+      wv[ht] = *reinterpret_cast<const v4f*>(p.w + (size_t)t * p.H_I + h0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[ht][i] = h0 + i < p.H_I ? p.w[(size_t)t * p.H_I + h0 + i] : 0.0f;
+    }
+  }
   const int seq = p.q_seq[t];
   const int pos = p.q_pos[t];
+  const int e_begin = chunk * kIdxChunk + wave * kIdxWaveEntries;
+  const bool seq_ok = seq >= 0 && seq < p.B;
+  // Page of every group (lane u < 16 fetches group u's page id); a group of
+  // 16 never straddles a page because the page size is a multiple of 16.
+  int my_page = -1;
+  if (seq_ok && lane < kIdxGroups) {
+    const int pi = (e_begin + 16 * lane) / p.page_size;
+    if (pi < p.max_pages) my_page = p.page_table[(size_t)seq * p.max_pages + pi];
+  }
   int nv = 0;
-  if (seq >= 0 && seq < p.B && pos >= 0) nv = min(pos / p.ratio_m, p.n_comp[seq]);
+  if (seq_ok && pos >= 0) nv = min(pos / p.ratio_m, p.n_comp[seq]);
   nv = max(0, min(nv, (int)min<int64_t>(p.ld, 0x7fffffff)));
   if (chunk == 0 && threadIdx.x == 0) p.n_visible[t] = nv;
-  const int e_begin = chunk * kIdxChunk + wave * kIdxWaveEntries;
   if (e_begin >= nv) return;
   const int e_end = min(nv, e_begin + kIdxWaveEntries);
 
-  // Page of every group first (lane u < 16 fetches group u's page id: one
-  // round trip), then all key loads back to back.  Group u covers entries
-  // e_begin + 16 u + (0..15); lane (g, r) loads entry r's dims [32g, 32g+32).
-  const bool dim_ok = 32 * g < p.D_I;
-  const int32_t* pt = p.page_table + (size_t)seq * p.max_pages;
-  int my_page = -1;
-  {
-    const int e0 = e_begin + 16 * lane;
-    if (lane < kIdxGroups && e0 < e_end) {
-      const int pi = e0 / p.page_size;
-      if (pi < p.max_pages) my_page = pt[pi];
-    }
-  }
+  // ---- all key loads back to back.  Group u covers entries
+  // e_begin + 16 u + (0..15); lane (g, r) loads entry r's dims [32 g, 32 g + 32).
   int poff = e_begin % p.page_size;        // uniform: offset of group u in its page
   v8i kb[kIdxGroups];
   uint32_t ok_mask = 0;                    // uniform: group has a valid page
@@ -80,43 +102,32 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
     poff += 16;
     if (poff >= p.page_size) poff -= p.page_size;
   }
-
-  // Query operand: 4 tiles of 16 index heads; lane holds head 16*ht + r,
-  // dims [32g, 32g+32).  Weights for output rows (heads 16*ht + 4g + i).
-  v8i qa[4];
-  float wv[4][4];
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const int h = 16 * ht + r;
-    if (h < p.H_I && dim_ok) {
-      const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
-      const v4i lo = ld16(src), hi = ld16(src + 16);
-      qa[ht] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      qa[ht] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * ht + 4 * g + i;
-      wv[ht][i] = hh < p.H_I ? p.w[(size_t)t * p.H_I + hh] * p.qk_scale : 0.0f;
-    }
-  }
+  for (int ht = 0; ht < 4; ++ht) wv[ht] *= p.qk_scale;
   const int n_ht = (p.H_I + 15) >> 4;
 
+  // ---- software pipeline: the MFMAs of group u + 1 go out before the
+  // weighted ReLU of group u; the head sum runs as four independent chains
   float* out = p.scores + (size_t)t * p.ld;
+  auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+      acc[ht] = ht < n_ht ? mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f}) : (v4f){0.f, 0.f, 0.f, 0.f};
+  };
+  v4f acc[2][4];
+  mfmas(kb[0], acc[0]);
 #pragma unroll
   for (int u = 0; u < kIdxGroups; ++u) {
-    const int e = e_begin + 16 * u + r;
-    float part = 0.0f;
+    if (u + 1 < kIdxGroups) mfmas(kb[u + 1], acc[(u + 1) & 1]);
+    float pp[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
-      if (ht < n_ht) {
-        const v4f acc = mfma_f8_128(qa[ht], kb[u], (v4f){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part += wv[ht][i] * fmaxf(acc[i], 0.0f);
-      }
+      const v4f a = acc[u & 1][ht];
+      pp[ht] = wv[ht][0] * fmaxf(a[0], 0.0f) + wv[ht][1] * fmaxf(a[1], 0.0f) +
+               (wv[ht][2] * fmaxf(a[2], 0.0f) + wv[ht][3] * fmaxf(a[3], 0.0f));
     }
-    part = sum_over_groups(part);
+    const float part = sum_over_groups((pp[0] + pp[1]) + (pp[2] + pp[3]));
+    const int e = e_begin + 16 * u + r;
     if (g == 0 && e < e_end) out[e] = ((ok_mask >> u) & 1u) ? part : -__builtin_inff();
   }
 }
