@@ -153,10 +153,9 @@ int csa_index_scores(const uint8_t* q_idx, float q_idx_scale, const float* w, co
   p.H_I = H_I;
   p.D_I = D_I;
   p.ratio_m = ratio_m;
-  p.chunk = index_chunk_entries();
-  const int64_t n_chunks = ceil_div(std::min<int64_t>(ld_scores, (int64_t)max_pages * page_size), p.chunk);
-  p.n_chunks = (int)std::max<int64_t>(1, n_chunks);
-  if ((int64_t)T * p.n_chunks >= ((int64_t)1 << 31)) return CSA_ERR_UNSUPPORTED;
+  // entries per workgroup (and the grid) are chosen by the launcher
+  if ((int64_t)T * ceil_div(std::min<int64_t>(ld_scores, (int64_t)max_pages * page_size), 256) >= ((int64_t)1 << 31))
+    return CSA_ERR_UNSUPPORTED;
   return launch_status(launch_index_scores(p, (hipStream_t)stream));
 }
 

@@ -22,10 +22,9 @@ struct IndexParams {
   float qk_scale;     // q_idx_scale * k_idx_scale
   int num_pages, page_size, max_pages, B;
   int T, H_I, D_I, ratio_m;
-  int chunk, n_chunks;
+  int chunk, n_chunks;   // set by the launcher
 };
 hipError_t launch_index_scores(const IndexParams& p, hipStream_t stream);
-int index_chunk_entries();
 
 struct TopkParams {
   const float* scores;

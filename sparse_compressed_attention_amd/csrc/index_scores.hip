@@ -21,11 +21,17 @@
 #include "csa_device.h"
 #include "csa_internal.h"
 
+#include <algorithm>
+
 namespace csa {
 
 namespace {
 
 constexpr int kIdxWaves = 4;
+
+// max(x, 0) as one v_med3_f32 (fmaxf on an MFMA result costs a canonicalising
+// v_max first)
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
 constexpr int kIdxGroups = 16;                       // groups of 16 entries per wave
 constexpr int kIdxWaveEntries = 16 * kIdxGroups;     // 256
 constexpr int kIdxChunk = kIdxWaves * kIdxWaveEntries;
@@ -104,7 +110,6 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   }
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) wv[ht] *= p.qk_scale;
-  const int n_ht = (p.H_I + 15) >> 4;
 
   // ---- software pipeline: the MFMAs of group u + 1 go out before the
   // weighted ReLU of group u; the head sum runs as four independent chains
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
-      acc[ht] = ht < n_ht ? mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f}) : (v4f){0.f, 0.f, 0.f, 0.f};
+      acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});   // rows of absent heads are zero
   };
   v4f acc[2][4];
   mfmas(kb[0], acc[0]);
@@ -123,8 +128,7 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const v4f a = acc[u & 1][ht];
-      pp[ht] = wv[ht][0] * fmaxf(a[0], 0.0f) + wv[ht][1] * fmaxf(a[1], 0.0f) +
-               (wv[ht][2] * fmaxf(a[2], 0.0f) + wv[ht][3] * fmaxf(a[3], 0.0f));
+      pp[ht] = wv[ht][0] * relu(a[0]) + wv[ht][1] * relu(a[1]) + (wv[ht][2] * relu(a[2]) + wv[ht][3] * relu(a[3]));
     }
     const float part = sum_over_groups((pp[0] + pp[1]) + (pp[2] + pp[3]));
     const int e = e_begin + 16 * u + r;
@@ -132,14 +136,182 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   }
 }
 
-}  // namespace
+// ---- many queries of one sequence (prefill) -----------------------------
+// All queries scan the same compressed keys, so a workgroup of kMqQ waves
+// takes kMqQ queries (one per wave) and walks the whole key range in chunks
+// of 256 entries, each staged once in LDS and scored against all kMqQ
+// queries: the indexer becomes a GEMM [queries x heads] x [entries] whose
+// key tile is read from memory once per kMqQ queries.  The next chunk's keys
+// are loaded into registers while the current chunk is scored (LDS double
+// buffer); page ids run two chunks ahead.  LDS layout: the MFMA B operand of
+// group u (16 entries) for lane l at (u * 64 + l) * 32 bytes, so every lane
+// reads its 32 bytes contiguously.
+constexpr int kMqQ = 8;
+constexpr int kMqGroups = 16;
+constexpr int kMqChunk = 16 * kMqGroups;
+constexpr int kMqGpw = kMqGroups / kMqQ;    // groups loaded per wave per chunk
+static_assert(kMqGroups % kMqQ == 0, "groups split evenly over the waves");
 
-hipError_t launch_index_scores(const IndexParams& p, hipStream_t stream) {
-  const int blocks = p.T * p.n_chunks;
-  hipLaunchKernelGGL(index_scores_kernel, dim3(blocks), dim3(64 * kIdxWaves), 0, stream, p);
-  return hipPeekAtLastError();
+__global__ __launch_bounds__(64 * kMqQ, 1) void index_scores_mq_kernel(IndexParams p) {
+  __shared__ __attribute__((aligned(16))) v8i ks[2][kMqGroups * 64];
+  __shared__ uint32_t okw[2][kMqQ];
+  const int qb = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const bool dim_ok = 32 * g < p.D_I;
+  const int t = qb * kMqQ + wave;
+  const bool q_ok = t < p.T;
+
+  // ---- this wave's query operand and weights (layout as in the
+  // one-query kernel)
+  v8i qa[4];
+  v4f wv[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = 16 * ht + r;
+    qa[ht] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    if (q_ok && h < p.H_I && dim_ok) {
+      const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
+      const v4i lo = ld16(src), hi = ld16(src + 16);
+      qa[ht] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    const int h0 = 16 * ht + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[ht][i] = (q_ok && h0 + i < p.H_I) ? p.w[(size_t)t * p.H_I + h0 + i] : 0.0f;
+  }
+
+  // ---- visible counts of the workgroup's queries (all in sequence 0)
+  const int nc = p.n_comp[0];
+  int nv_max = 0, nv_own = 0;
+#pragma unroll
+  for (int w = 0; w < kMqQ; ++w) {
+    const int tw = qb * kMqQ + w;
+    int nv = 0;
+    if (tw < p.T) {
+      const int pos = p.q_pos[tw];
+      if (p.q_seq[tw] == 0 && pos >= 0) nv = min(pos / p.ratio_m, nc);
+      nv = max(0, min(nv, (int)min<int64_t>(p.ld, 0x7fffffff)));
+      if (w == wave && lane == 0) p.n_visible[tw] = nv;
+    }
+    nv_max = max(nv_max, nv);
+    if (w == wave) nv_own = nv;
+  }
+  const int n_ch = (nv_max + kMqChunk - 1) / kMqChunk;
+  if (n_ch == 0) return;                     // uniform over the workgroup
+
+  // page id of group (4 w + j) of chunk c, fetched by lane j (< kMqGpw)
+  auto load_page = [&](int c) -> int {
+    int pg = -1;
+    if (lane < kMqGpw && c < n_ch) {
+      const int pi = (c * kMqChunk + 16 * (kMqGpw * wave + lane)) / p.page_size;
+      if (pi < p.max_pages) pg = p.page_table[pi];
+    }
+    return pg;
+  };
+  // this wave's groups of chunk c: lane (g, r) entry r's dims [32 g, 32 g + 32)
+  auto load_keys = [&](int c, int pg, v8i (&kl)[kMqGpw], uint32_t& okbits) {
+    okbits = 0;
+#pragma unroll
+    for (int j = 0; j < kMqGpw; ++j) {
+      const int u = kMqGpw * wave + j;
+      const int eg = c * kMqChunk + 16 * u;
+      const int page = __builtin_amdgcn_readlane(pg, j);
+      const bool ok = eg < nv_max && page >= 0 && page < p.num_pages;
+      okbits |= (ok ? 1u : 0u) << u;
+      kl[j] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+      if (ok && dim_ok && eg + r < nv_max) {
+        const uint8_t* src = p.k_idx + ((size_t)page * p.page_size + eg % p.page_size + r) * p.D_I + 32 * g;
+        const v4i lo = ld16(src), hi = ld16(src + 16);
+        kl[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+  };
+  auto store_keys = [&](int b, const v8i (&kl)[kMqGpw], uint32_t okbits) {
+#pragma unroll
+    for (int j = 0; j < kMqGpw; ++j) ks[b][(kMqGpw * wave + j) * 64 + lane] = kl[j];
+    if (lane == 0) okw[b][wave] = okbits;
+  };
+
+  v8i kl[kMqGpw];
+  uint32_t okbits;
+  int pg_next = load_page(1);
+  {
+    const int pg0 = load_page(0);
+    load_keys(0, pg0, kl, okbits);
+  }
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) wv[ht] *= p.qk_scale;
+  store_keys(0, kl, okbits);
+  __syncthreads();
+
+  float* out = p.scores + (size_t)t * p.ld;
+  auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+      acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});   // rows of absent heads are zero
+  };
+
+  for (int c = 0; c < n_ch; ++c) {
+    const int b = c & 1;
+    // next chunk's keys into registers (page ids one chunk further ahead)
+    const bool more = c + 1 < n_ch;
+    if (more) {
+      load_keys(c + 1, pg_next, kl, okbits);
+      pg_next = load_page(c + 2);
+    }
+    const int e0 = c * kMqChunk;
+    if (q_ok && e0 < nv_own) {
+      uint32_t ok_mask = 0;
+#pragma unroll
+      for (int w = 0; w < kMqQ; ++w) ok_mask |= okw[b][w];
+      const int e_end = min(nv_own, e0 + kMqChunk);
+      // MFMAs of group u + 1 before the weighted ReLU of group u
+      v4f acc[2][4];
+      v8i kb = ks[b][lane];
+      mfmas(kb, acc[0]);
+#pragma unroll
+      for (int u = 0; u < kMqGroups; ++u) {
+        if (u + 1 < kMqGroups) {
+          kb = ks[b][(u + 1) * 64 + lane];
+          mfmas(kb, acc[(u + 1) & 1]);
+        }
+        float pp[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          const v4f a = acc[u & 1][ht];
+          pp[ht] = wv[ht][0] * relu(a[0]) + wv[ht][1] * relu(a[1]) + (wv[ht][2] * relu(a[2]) + wv[ht][3] * relu(a[3]));
+        }
+        const float part = sum_over_groups((pp[0] + pp[1]) + (pp[2] + pp[3]));
+        const int e = e0 + 16 * u + r;
+        if (g == 0 && e < e_end) out[e] = ((ok_mask >> u) & 1u) ? part : -__builtin_inff();
+      }
+    }
+    if (more) store_keys(b ^ 1, kl, okbits);
+    __syncthreads();
+  }
 }
 
-int index_chunk_entries() { return kIdxChunk; }
+}  // namespace
+
+hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
+  IndexParams p = p_in;
+  const int64_t span = std::min<int64_t>(p.ld, (int64_t)p.max_pages * p.page_size);
+  if (p.B == 1 && p.T >= 2 * kMqQ) {
+    // one sequence, many queries: key tiles shared through LDS
+    p.chunk = kMqChunk;
+    p.n_chunks = (int)std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
+    const int64_t blocks = (int64_t)((p.T + kMqQ - 1) / kMqQ);
+    hipLaunchKernelGGL(index_scores_mq_kernel, dim3((unsigned)blocks), dim3(64 * kMqQ), 0, stream, p);
+    return hipPeekAtLastError();
+  }
+  p.chunk = kIdxChunk;
+  p.n_chunks = (int)std::max<int64_t>(1, (span + kIdxChunk - 1) / kIdxChunk);
+  const int64_t blocks = (int64_t)p.T * p.n_chunks;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(index_scores_kernel, dim3((unsigned)blocks), dim3(64 * kIdxWaves), 0, stream, p);
+  return hipPeekAtLastError();
+}
 
 }  // namespace csa
