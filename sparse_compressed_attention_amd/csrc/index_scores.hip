@@ -152,10 +152,14 @@ constexpr int kMqChunk = 16 * kMqGroups;
 constexpr int kMqGpw = kMqGroups / kMqQ;    // groups loaded per wave per chunk
 static_assert(kMqGroups % kMqQ == 0, "groups split evenly over the waves");
 
-__global__ __launch_bounds__(64 * kMqQ, 1) void index_scores_mq_kernel(IndexParams p) {
+__global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexParams p, int n_split) {
   __shared__ __attribute__((aligned(16))) v8i ks[2][kMqGroups * 64];
   __shared__ uint32_t okw[2][kMqQ];
-  const int qb = blockIdx.x;
+  // workgroup = (query block, part of the key range): n_split parts so that
+  // a CU runs two workgroups (four waves per SIMD) and the MFMAs of one wave
+  // overlap the weighted-ReLU work of another
+  const int qb = blockIdx.x / n_split;
+  const int split = blockIdx.x - qb * n_split;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -193,13 +197,16 @@ __global__ __launch_bounds__(64 * kMqQ, 1) void index_scores_mq_kernel(IndexPara
       const int pos = p.q_pos[tw];
       if (p.q_seq[tw] == 0 && pos >= 0) nv = min(pos / p.ratio_m, nc);
       nv = max(0, min(nv, (int)min<int64_t>(p.ld, 0x7fffffff)));
-      if (w == wave && lane == 0) p.n_visible[tw] = nv;
+      if (split == 0 && w == wave && lane == 0) p.n_visible[tw] = nv;
     }
     nv_max = max(nv_max, nv);
     if (w == wave) nv_own = nv;
   }
-  const int n_ch = (nv_max + kMqChunk - 1) / kMqChunk;
-  if (n_ch == 0) return;                     // uniform over the workgroup
+  const int n_all = (nv_max + kMqChunk - 1) / kMqChunk;
+  const int per = (n_all + n_split - 1) / n_split;
+  const int c_begin = split * per;
+  const int n_ch = min(n_all, c_begin + per);   // chunks [c_begin, n_ch) of this workgroup
+  if (c_begin >= n_ch) return;                  // uniform over the workgroup
 
   // page id of group (4 w + j) of chunk c, fetched by lane j (< kMqGpw)
   auto load_page = [&](int c) -> int {
@@ -236,10 +243,10 @@ __global__ __launch_bounds__(64 * kMqQ, 1) void index_scores_mq_kernel(IndexPara
 
   v8i kl[kMqGpw];
   uint32_t okbits;
-  int pg_next = load_page(1);
+  int pg_next = load_page(c_begin + 1);
   {
-    const int pg0 = load_page(0);
-    load_keys(0, pg0, kl, okbits);
+    const int pg0 = load_page(c_begin);
+    load_keys(c_begin, pg0, kl, okbits);
   }
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) wv[ht] *= p.qk_scale;
@@ -253,8 +260,8 @@ __global__ __launch_bounds__(64 * kMqQ, 1) void index_scores_mq_kernel(IndexPara
       acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});   // rows of absent heads are zero
   };
 
-  for (int c = 0; c < n_ch; ++c) {
-    const int b = c & 1;
+  for (int c = c_begin; c < n_ch; ++c) {
+    const int b = (c - c_begin) & 1;
     // next chunk's keys into registers (page ids one chunk further ahead)
     const bool more = c + 1 < n_ch;
     if (more) {
@@ -302,8 +309,12 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
     // one sequence, many queries: key tiles shared through LDS
     p.chunk = kMqChunk;
     p.n_chunks = (int)std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
-    const int64_t blocks = (int64_t)((p.T + kMqQ - 1) / kMqQ);
-    hipLaunchKernelGGL(index_scores_mq_kernel, dim3((unsigned)blocks), dim3(64 * kMqQ), 0, stream, p);
+    const int64_t n_qb = (p.T + kMqQ - 1) / kMqQ;
+    const int64_t span_ch = std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
+    // about two workgroups per CU (256 CUs), parts of at least 4 chunks
+    const int n_split = (int)std::max<int64_t>(1, std::min<int64_t>((512 + n_qb - 1) / n_qb, span_ch / 4));
+    hipLaunchKernelGGL(index_scores_mq_kernel, dim3((unsigned)(n_qb * n_split)), dim3(64 * kMqQ), 0, stream, p,
+                       n_split);
     return hipPeekAtLastError();
   }
   p.chunk = kIdxChunk;
