@@ -215,8 +215,18 @@ __global__ __launch_bounds__(kTopkBlock) void topk_chunk_kernel(TopkParams p) {
   const int cnt = max(0, min(SEG, n - i0));
   const float* src = p.scores + (size_t)t * p.ld + c0 + i0;
   uint32_t key[SEG];
+  if (cnt == SEG && ((((uintptr_t)src) & 15) == 0)) {
+    // whole segment: 16-byte loads
 #pragma unroll
-  for (int j = 0; j < SEG; ++j) key[j] = j < cnt ? float_order_key(src[j]) : 0u;
+    for (int j = 0; j < SEG; j += 4) {
+      const v4f v = *reinterpret_cast<const v4f*>(src + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[j + e] = float_order_key(v[e]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) key[j] = j < cnt ? float_order_key(src[j]) : 0u;
+  }
   const uint32_t valid = cnt >= 32 ? 0xffffffffu : ((1u << cnt) - 1u);
   const int K = min(p.k, n);
   if (p.n_chunks == 1) {
@@ -260,16 +270,33 @@ __global__ __launch_bounds__(kTopkBlock) void topk_merge_kernel(TopkParams p) {
   uint32_t key[SEG];
   int32_t idx[SEG];
   uint32_t valid = 0u;
+  const uint32_t* ksrc = p.cand_key + base + i0;
+  const int32_t* isrc = p.cand_idx + base + i0;
+  if (i0 + SEG <= ncand && ((((uintptr_t)ksrc) | ((uintptr_t)isrc)) & 15) == 0) {
+    // whole segment: 16-byte loads
 #pragma unroll
-  for (int j = 0; j < SEG; ++j) {
-    key[j] = 0u;
-    idx[j] = -1;
-    if (i0 + j < ncand) {
-      key[j] = p.cand_key[base + i0 + j];
-      idx[j] = p.cand_idx[base + i0 + j];
+    for (int j = 0; j < SEG; j += 4) {
+      const v4i kv = *reinterpret_cast<const v4i*>(ksrc + j);
+      const v4i iv = *reinterpret_cast<const v4i*>(isrc + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[j + e] = (uint32_t)kv[e];
+        idx[j + e] = iv[e];
+      }
     }
-    valid |= (idx[j] >= 0 ? 1u : 0u) << j;
+  } else {
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+      key[j] = 0u;
+      idx[j] = -1;
+      if (i0 + j < ncand) {
+        key[j] = ksrc[j];
+        idx[j] = isrc[j];
+      }
+    }
   }
+#pragma unroll
+  for (int j = 0; j < SEG; ++j) valid |= (idx[j] >= 0 ? 1u : 0u) << j;
   int total;
   block_exclusive_scan(__builtin_popcount(valid), sh, &total);
   const int K = min(p.k, total);
