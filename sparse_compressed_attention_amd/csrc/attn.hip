@@ -671,14 +671,14 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         const v2i pk = (v2i){(int)pack2_bf16(v[0] * invL, v[1] * invL), (int)pack2_bf16(v[2] * invL, v[3] * invL)};
         *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + dim) = pk;
       } else {
-        *reinterpret_cast<v4f*>(p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + 2) + dim) = v;
+        *reinterpret_cast<v4f*>(p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + kPartPad) + dim) = v;
       }
     }
     if (DH == 0 && g == 0) {
       if (final_out) {
         if (p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
       } else {
-        float* dst = p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + 2) + D;
+        float* dst = p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + kPartPad) + D;
         dst[0] = M;
         dst[1] = L;
       }
@@ -741,39 +741,70 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
 }
 
 // Combines the per-split partial states (unnormalised O, running max in log2
-// units, denominator) of every (query, head) into the output and lse.
+// units, denominator) of every (query, head) into the output and lse.  128
+// threads per (query, head): the split weights exp2(M_s - M) are computed
+// once into LDS (thread s owns split s), then thread i sums dims
+// [4 i, 4 i + 4) over the splits with 16-byte loads.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+  __shared__ float wgt[2][kAttnMaxSplits];
+  __shared__ float red[2][2][2];
   const int D = p.D_nope + p.D_rope;
-  const int tpd = D / 4;
-  const int hpb = 256 / tpd;
-  const int pair = blockIdx.x * hpb + threadIdx.x / tpd;
-  if (threadIdx.x >= hpb * tpd || pair >= p.T * p.H) return;
-  const int t = pair / p.H;
-  const int h = pair - t * p.H;
-  const int d0 = (threadIdx.x % tpd) * 4;
+  const int RS = D + kPartPad;
+  const int half = threadIdx.x >> 7;          // pair of this thread within the workgroup
+  const int sub = threadIdx.x & 127;
+  const int wv = (threadIdx.x >> 6) & 1;      // wave within the pair
+  const int pair = blockIdx.x * 2 + half;
+  const bool pair_ok = pair < p.T * p.H;
+  const int t = pair_ok ? pair / p.H : 0;
+  const int h = pair_ok ? pair - t * p.H : 0;
   const bool prefill = p.prefill_seq >= 0;
   const int seq = prefill ? p.prefill_seq : t;
   const int pos = p.q_pos[t];
   const int nv = pos >= 0 ? max(0, min(pos / p.ratio_m, p.n_comp[seq])) : 0;
   const int n_slots = (((p.topk ? p.k : nv) + kAttnTile - 1) & ~(kAttnTile - 1)) + p.W;
   const int used = max(1, min(p.n_splits, (n_slots + p.per_split - 1) / p.per_split));
-  float M = -__builtin_inff();
-  for (int s = 0; s < used; ++s) M = fmaxf(M, p.part[(((size_t)s * p.T + t) * p.H + h) * (D + 2) + D]);
-  const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
-  float L = 0.0f;
-  v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < used; ++s) {
-    const float* src = p.part + (((size_t)s * p.T + t) * p.H + h) * (D + 2);
-    const float ms = src[D];
-    const float a = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - Ms);
-    L += src[D + 1] * a;
-    const v4f v = *reinterpret_cast<const v4f*>(src + d0);
-    acc += v * a;
+  const size_t pstride = (size_t)p.T * p.H * RS;   // one split
+  const float* row = p.part + ((size_t)t * p.H + h) * RS;
+
+  // split weights and the merged max / denominator
+  float m = -__builtin_inff(), l = 0.0f;
+  if (pair_ok && sub < used) {
+    m = row[sub * pstride + D];
+    l = row[sub * pstride + D + 1];
   }
+  float mm = m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
+  if ((threadIdx.x & 63) == 0) red[half][0][wv] = mm;
+  __syncthreads();
+  const float M = fmaxf(red[half][0][0], red[half][0][1]);
+  const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
+  const float a = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Ms);
+  if (sub < kAttnMaxSplits) wgt[half][sub] = a;
+  float la = l * a;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) la += __shfl_xor(la, off, 64);
+  if ((threadIdx.x & 63) == 0) red[half][1][wv] = la;
+  __syncthreads();
+  const float L = red[half][1][0] + red[half][1][1];
+  if (!pair_ok) return;
   const float invL = L > 0.0f ? 1.0f / L : 0.0f;
-  *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + d0) =
-      (v2i){(int)pack2_bf16(acc[0] * invL, acc[1] * invL), (int)pack2_bf16(acc[2] * invL, acc[3] * invL)};
-  if (d0 == 0 && p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
+  const int d0 = 4 * sub;
+  if (d0 < D) {
+    v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 4 <= used; s += 4) {
+      v4f v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const v4f*>(row + (s + j) * pstride + d0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += v[j] * wgt[half][s + j];
+    }
+    for (; s < used; ++s) acc += *reinterpret_cast<const v4f*>(row + s * pstride + d0) * wgt[half][s];
+    *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + d0) =
+        (v2i){(int)pack2_bf16(acc[0] * invL, acc[1] * invL), (int)pack2_bf16(acc[2] * invL, acc[3] * invL)};
+  }
+  if (sub == 0 && p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
 }
 
 template <int DN, int DR>
@@ -783,9 +814,8 @@ hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((attn_kernel<DN, DR>), dim3(blocks), dim3(256), 0, stream, p);
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  const int D = DN + DR;
-  const int hpb = 256 / (D / 4);
-  const int mblocks = (p.T * p.H + hpb - 1) / hpb;
+  static_assert((DN + DR) / 4 <= 128, "one 128-thread team per (query, head)");
+  const int mblocks = (p.T * p.H + 1) / 2;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(mblocks), dim3(256), 0, stream, p);
   return hipPeekAtLastError();
 }

@@ -54,7 +54,7 @@ struct AttnPlan {
   size_t ws_bytes = 0;
 };
 size_t partial_bytes(int64_t T, int64_t H, int D, int splits) {
-  return (size_t)splits * (size_t)T * (size_t)H * (size_t)(D + 2) * sizeof(float);
+  return (size_t)splits * (size_t)T * (size_t)H * (size_t)(D + kPartPad) * sizeof(float);
 }
 // Preferred plan, then shrunk to what `ws_avail` holds.  Returns false when
 // even the minimum number of splits does not fit.
@@ -64,9 +64,11 @@ bool plan_attn(int64_t T, int32_t H, int D, int64_t max_slots, size_t ws_avail, 
   // the kernel pads the selected slots to whole tiles (at most kAttnTile - 1 more)
   const int64_t slots = std::max<int64_t>(1, max_slots + kAttnTile - 1);
   const int64_t min_splits = ceil_div(slots, kAttnMaxSlots);
+  if (min_splits > kAttnMaxSplits) return false;   // key range beyond what one merge combines
   const int64_t base = std::max<int64_t>(1, T * pl.n_hg);
   int64_t splits = std::max<int64_t>(min_splits, ceil_div(kTargetBlocks, base));
   splits = std::min<int64_t>(splits, ceil_div(slots, kAttnTile));
+  splits = std::min<int64_t>(splits, kAttnMaxSplits);
   splits = std::max<int64_t>(splits, min_splits);
   if (limit_ws && splits > 1) {
     const size_t one = partial_bytes(T, H, D, 1);
@@ -217,6 +219,7 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
     p.ps_magic = (uint64_t)((num + (unsigned)p.page_size - 1) / (unsigned)p.page_size);
     p.ps_shift = 32 + l;
   }
+  if (max_slots + kAttnTile - 1 > (int64_t)kAttnMaxSplits * kAttnMaxSlots) return CSA_ERR_UNSUPPORTED;
   AttnPlan pl;
   const size_t avail = (workspace && aligned16(workspace)) ? workspace_bytes : 0;
   if (!plan_attn(p.T, p.H, p.D_nope + p.D_rope, max_slots, avail, true, &pl)) return CSA_ERR_WORKSPACE;

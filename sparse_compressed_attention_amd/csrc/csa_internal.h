@@ -56,7 +56,7 @@ struct AttnParams {
   const float* sink;
   uint16_t* out;
   float* lse;
-  float* part;             // [n_splits][T][H][D + 2] or nullptr
+  float* part;             // [n_splits][T][H][D + kPartPad] or nullptr: O, then (M, L) at D, D + 1
   float lat_scale, swa_scale;
   float sm_scale;          // softmax scale (natural-log units)
   // derived on the host (uniform): sm_scale*log2(e); FP8 probability scale
@@ -78,5 +78,7 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
 constexpr int kAttnMaxSlots = 2048;   // key slots one workgroup handles
 constexpr int kAttnTau = 4;           // lazy-rescale threshold (log2 units)
 constexpr int kAttnTile = 64;
+constexpr int kAttnMaxSplits = 128;   // splits of one query's key slots
+constexpr int kPartPad = 4;           // partial rows padded to 16 bytes
 
 }  // namespace csa

@@ -60,9 +60,12 @@ def test_workspace_sizes(lib):
     assert csa.csa_topk_workspace_size(1, 1 << 22, 2048) == 0
     # many queries: one workgroup per (query, 32 heads), no split
     assert csa.csa_attn_workspace_size(64, 128, 448, 64, 640) == 0
-    # one query: split over workgroups, partials of 514 floats per head
+    # one query: split over workgroups, partials of 512 + 2 floats per head
+    # padded to 516 (16-byte rows)
     ws = csa.csa_attn_workspace_size(1, 128, 448, 64, 640)
-    assert ws > 0 and ws % (128 * 514 * 4) == 0
+    assert ws > 0 and ws % (128 * 516 * 4) == 0
+    # key ranges beyond 128 splits of 2048 slots are not supported
+    assert csa.csa_attn_workspace_size(1, 128, 448, 64, 128 * 2048) == 0
     assert csa.csa_attn_workspace_size(1, 128, 100, 64, 640) == 0   # unsupported dims
 
 
