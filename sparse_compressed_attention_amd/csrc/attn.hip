@@ -157,7 +157,7 @@ struct Block {
   int n_sel, sel_end, kv0, nkeys;   // slots: [0, n_sel) selected, [sel_end, sel_end + W) window
 };
 
-template <int DN, int DR, int DH>
+template <int DN, int DR, int DH, int HT>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, uint8_t* xs0, int32_t* desc,
                                           v4f* sx, int wave) {
   using C = Cfg<DN, DR>;
@@ -166,9 +166,11 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int r = lane & 15;
-  const int ht = wave & 1;
-  const int h = bk.hg * 32 + ht * 16 + r;
-  const bool tile_ok = bk.hg * 32 + ht * 16 < p.H;
+  constexpr int kWaves = 2 * HT;              // waves (head tile, dim half)
+  constexpr int kThreads = 64 * kWaves;
+  const int ht = wave % HT;
+  const int h = bk.hg * (16 * HT) + ht * 16 + r;
+  const bool tile_ok = bk.hg * (16 * HT) + ht * 16 < p.H;
   const bool head_ok = h < p.H;
   const bool prefill = p.prefill_seq >= 0;
   const int t = bk.t, seq = bk.seq, kv0 = bk.kv0, nkeys = bk.nkeys, n_sel = bk.n_sel, sel_end = bk.sel_end;
@@ -205,11 +207,11 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   // skip.  First-level loads (top-k index or ring position) need nothing
   // loaded before them; then all page-table loads: two round trips.
   const int32_t* pt = p.page_table + (size_t)seq * p.max_pages;
-  constexpr int kSPT = kAttnMaxSlots / 256;   // slots per thread
+  constexpr int kSPT = kAttnMaxSlots / kThreads;   // slots per thread
   int v1[kSPT];
 #pragma unroll
   for (int j = 0; j < kSPT; ++j) {
-    const int s = threadIdx.x + 256 * j;
+    const int s = threadIdx.x + kThreads * j;
     const int slot = kv0 + s;
     int v = -1;
     if (s < nkeys) {
@@ -224,7 +226,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   int v2[kSPT];
 #pragma unroll
   for (int j = 0; j < kSPT; ++j) {
-    const int s = threadIdx.x + 256 * j;
+    const int s = threadIdx.x + kThreads * j;
     const int idx = v1[j];
     int page = -1;
     if (s < nkeys && kv0 + s < n_sel && idx >= 0) {
@@ -236,7 +238,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   const int pos = bk.pos;
 #pragma unroll
   for (int j = 0; j < kSPT; ++j) {
-    const int s = threadIdx.x + 256 * j;
+    const int s = threadIdx.x + kThreads * j;
     if (s >= nkeys) continue;
     const int slot = kv0 + s;
     int d = -1;
@@ -266,7 +268,9 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   // every wave issues the same number of DMAs per tile; those rows are
   // cleared in LDS before use.
   const int dcc = lane >> 4;
-  const int dkey = 16 * wave + ((lane & 15) ^ (((wave ^ dcc) & 1) << 3));
+  const int drg = wave & 3;                   // row group (16 keys) this wave copies
+  const int dq0 = wave >> 2;                  // first quad; then every kQStep-th
+  const int dkey = 16 * drg + ((lane & 15) ^ (((drg ^ dcc) & 1) << 3));
   const uint8_t* tsrc_n = p.lat_nope;   // this lane's row of the tile being issued
   const uint8_t* tsrc_r = reinterpret_cast<const uint8_t*>(p.lat_rope);
   auto prep_tile = [&](int tile) {
@@ -287,14 +291,17 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     tsrc_n = nsrc;
     tsrc_r = rsrc;
   };
+  constexpr int kQStep = kWaves / 4;                 // waves sharing a row group
+  constexpr int kQMax = (C::NQ + kQStep - 1) / kQStep;  // quads per wave (at most)
   constexpr int kParts = 3;                          // a tile's DMAs go out in three parts
-  constexpr int kPerPart = (C::NQ + kParts - 1) / kParts;
+  constexpr int kPerPart = (kQMax + kParts - 1) / kParts;
   auto issue_quads = [&](int buf, int part) {
     const uint32_t lds_base =
-        (uint32_t)(uintptr_t)(CSA_LDS uint8_t*)(xs0 + buf * C::TILE_BYTES) + (uint32_t)wave * 1024u;
+        (uint32_t)(uintptr_t)(CSA_LDS uint8_t*)(xs0 + buf * C::TILE_BYTES) + (uint32_t)drg * 1024u;
 #pragma unroll
     for (int q = 0; q < C::NQ; ++q) {
-      if (part >= 0 && q / kPerPart != part) continue;
+      if (q % kQStep != dq0) continue;
+      if (part >= 0 && (q / kQStep) / kPerPart != part) continue;
       const int c = 4 * q + dcc;
       const uint8_t* src;
       if (4 * q < C::CHNP) {
@@ -396,14 +403,14 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     rp_off[u][1] = rb_ * 256 + key_part(32 * u + kappa(g, 4 + (r >> 2)), rb_) + 8 * (r & 1);
   }
   v4f* sx_own = sx + (size_t)wave * 4 * 64 + lane;
-  const v4f* sx_oth = sx + (size_t)(wave ^ 2) * 4 * 64 + lane;
+  const v4f* sx_oth = sx + (size_t)((wave + HT) % kWaves) * 4 * 64 + lane;
 
   int buf = 0;
   for (int it = 0; it < n_tiles; ++it, buf = (buf + 1 == kNBuf) ? 0 : buf + 1) {
     // tile `it` landed in LDS (this wave's DMAs), then everyone's (barrier);
     // the barrier also retires every wave's reads of the buffer reused next
     asm volatile("" ::: "memory");
-    if (it + 1 < n_tiles) wait_vmcnt<C::NQ>(); else wait_vmcnt<0>();
+    if (it + 1 < n_tiles) wait_vmcnt<C::NQ / kQStep>(); else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const bool refill = it + 2 < n_tiles;
@@ -424,7 +431,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
       if (!((vmask >> dkey) & 1ull)) {
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q)
-          *reinterpret_cast<v4i*>(xb + (q * 4 + wave) * 1024 + 16 * lane) = (v4i){0, 0, 0, 0};
+          if (q % kQStep == dq0) *reinterpret_cast<v4i*>(xb + (q * 4 + drg) * 1024 + 16 * lane) = (v4i){0, 0, 0, 0};
       }
       lds_barrier();
     }
@@ -686,12 +693,16 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   }
 }
 
-template <int DN, int DR>
-__global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
+// HT = 16-head tiles per workgroup: 2 (4 waves, one per SIMD) when there are
+// few queries, 4 (8 waves, two per SIMD, each tile shared by 64 heads) when
+// there are enough (query, head group) pairs to fill the GPU without
+// splitting key ranges.
+template <int DN, int DR, int HT>
+__global__ __launch_bounds__(128 * HT, 1) void attn_kernel(AttnParams p) {
   using C = Cfg<DN, DR>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf * C::TILE_BYTES];
   __shared__ int32_t desc[kAttnMaxSlots];
-  __shared__ v4f sx[4 * 4 * 64];   // partial score tiles, [wave][subtile][lane]
+  __shared__ v4f sx[2 * HT * 4 * 64];   // partial score tiles, [wave][subtile][lane]
 
   // ---- which (query, head group, split).  Workgroups go to the 8 XCDs
   // round-robin by id.  With 8 or more queries, queries are spread over the
@@ -733,11 +744,11 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnParams p) {
   bk.nkeys = max(0, min(n_slots, bk.kv0 + p.per_split) - bk.kv0);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __builtin_assume(wave >= 0 && wave < 4);
-  if (wave >= 2)
-    attn_wave<DN, DR, 1>(p, bk, xs, desc, sx, wave);
+  __builtin_assume(wave >= 0 && wave < 2 * HT);
+  if (wave >= HT)
+    attn_wave<DN, DR, 1, HT>(p, bk, xs, desc, sx, wave);
   else
-    attn_wave<DN, DR, 0>(p, bk, xs, desc, sx, wave);
+    attn_wave<DN, DR, 0, HT>(p, bk, xs, desc, sx, wave);
 }
 
 // Combines the per-split partial states (unnormalised O, running max in log2
@@ -811,7 +822,10 @@ template <int DN, int DR>
 hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
   const int nb = p.n_hg * p.n_splits;
   const int blocks = (p.T >= 8 ? ((p.T + 7) / 8) * 8 : p.T) * nb;
-  hipLaunchKernelGGL((attn_kernel<DN, DR>), dim3(blocks), dim3(256), 0, stream, p);
+  if (p.ht == 4)
+    hipLaunchKernelGGL((attn_kernel<DN, DR, 4>), dim3(blocks), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<DN, DR, 2>), dim3(blocks), dim3(256), 0, stream, p);
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   static_assert((DN + DR) / 4 <= 128, "one 128-thread team per (query, head)");

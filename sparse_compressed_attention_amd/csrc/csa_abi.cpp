@@ -50,7 +50,7 @@ TopkPlan plan_topk(int32_t T, int64_t ld, int32_t k) {
 // ---- attention split of the key range over workgroups ---------------------
 constexpr int kTargetBlocks = 256;   // one workgroup per CU on MI355X
 struct AttnPlan {
-  int n_hg = 0, n_splits = 1, per_split = 0;
+  int ht = 2, n_hg = 0, n_splits = 1, per_split = 0;
   size_t ws_bytes = 0;
 };
 size_t partial_bytes(int64_t T, int64_t H, int D, int splits) {
@@ -60,7 +60,11 @@ size_t partial_bytes(int64_t T, int64_t H, int D, int splits) {
 // even the minimum number of splits does not fit.
 bool plan_attn(int64_t T, int32_t H, int D, int64_t max_slots, size_t ws_avail, bool limit_ws, AttnPlan* out) {
   AttnPlan pl;
-  pl.n_hg = (int)ceil_div(H, 32);
+  // 64 heads per workgroup (two waves per SIMD) when that alone gives a
+  // workgroup per CU, else 32 heads per workgroup and, if still too few,
+  // split key ranges
+  pl.ht = (T * ceil_div(H, 64) >= kTargetBlocks) ? 4 : 2;
+  pl.n_hg = (int)ceil_div(H, 16 * pl.ht);
   // the kernel pads the selected slots to whole tiles (at most kAttnTile - 1 more)
   const int64_t slots = std::max<int64_t>(1, max_slots + kAttnTile - 1);
   const int64_t min_splits = ceil_div(slots, kAttnMaxSlots);
@@ -223,6 +227,7 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
   AttnPlan pl;
   const size_t avail = (workspace && aligned16(workspace)) ? workspace_bytes : 0;
   if (!plan_attn(p.T, p.H, p.D_nope + p.D_rope, max_slots, avail, true, &pl)) return CSA_ERR_WORKSPACE;
+  p.ht = pl.ht;
   p.n_hg = pl.n_hg;
   p.n_splits = pl.n_splits;
   p.per_split = pl.per_split;

@@ -72,6 +72,7 @@ struct AttnParams {
   int swa_first_pos, swa_len;
   int T, H;
   int D_nope, D_rope;
+  int ht;                  // 16-head tiles per workgroup (2 or 4)
   int n_hg, n_splits, per_split;
 };
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);

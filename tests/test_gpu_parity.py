@@ -101,6 +101,23 @@ def test_prefill_small():
     check_full(ci.generate(spec, seed=104), queries=[0, 1, 17, 33, 50, 69])
 
 
+def test_prefill_64_head_workgroups():
+    # 160 queries x 2 groups of 64 heads fill the GPU without splitting the
+    # key range, so the launch uses 64-head (8-wave) workgroups
+    say("case prefill 64-head workgroups")
+    spec = ci.Spec(name="prefill_160", kind="prefill", ctx_lens=[6000], T_prefill=160)
+    check_full(ci.generate(spec, seed=111), queries=[0, 1, 63, 64, 100, 158, 159])
+
+
+def test_tiny_dims_64_head_workgroups():
+    # tiny dims (8 heads: one valid head tile of four, 48 + 16 latent) in
+    # 64-head workgroups: three idle head tiles, page size 16, ragged tails
+    say("case tiny dims 64-head workgroups")
+    spec = ci.Spec(name="tiny_prefill_260", kind="prefill", ctx_lens=[2000], T_prefill=260, H=8, D_nope=48,
+                   D_rope=16, H_I=4, D_I=32, k=16, W=32, page_size=16)
+    check_full(ci.generate(spec, seed=112), queries=[0, 5, 130, 255, 259])
+
+
 def test_ring_permutation_invariance_gpu():
     say("case ring permutation")
     wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1800]), seed=105)
