@@ -122,17 +122,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
-// (lgkmcnt(0)) but leaves the tile DMAs in flight, unlike __syncthreads,
-// which also drains vmcnt.  The empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt unchanged
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // One global_load_lds_dwordx4: every lane copies 16 bytes from `src` to LDS
 // byte address lds_base + 16 * lane.  Issued through asm so that the
 // compiler's wait-count pass does not see an LDS write in flight: left to

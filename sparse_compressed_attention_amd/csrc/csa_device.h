@@ -54,6 +54,18 @@ __device__ __forceinline__ v4f mfma_bf16_32(const v8bf& a, const v8bf& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ---- workgroup barrier for LDS traffic only -----------------------------
+// Waits for this wave's LDS accesses (lgkmcnt(0)) but leaves global loads
+// and LDS DMAs in flight, unlike __syncthreads, which also drains vmcnt.
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt unchanged
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- cross-lane reductions over the four 16-lane groups ------------------
 // v_permlane32_swap(a, b) returns (a, b) with the upper half's a swapped
 // for the lower half's b: lanes 0..31 get (a, a[l + 32]), lanes 32..63 get

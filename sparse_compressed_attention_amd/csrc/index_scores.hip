@@ -7,17 +7,20 @@
 // tensor units in FP8 over every visible compressed entry.
 //
 // Mapping on gfx950: one workgroup (4 waves) scores one query row over a
-// chunk of 1024 entries; each wave owns 256 consecutive entries = 16 groups
-// of 16.  Per group a wave runs one v_mfma 16x16x128 FP8 per 16 index heads:
-// A = the query's index heads (rows) x 128 dims, held in registers for the
-// whole chunk; B = 16 entry keys x 128 dims, loaded straight from HBM into
-// the operand registers (each key byte is used once, so no LDS staging).
-// The pages of the wave's 16 groups come from one vector load (lane u
-// fetches group u's page id; a group of 16 never straddles a page because the
-// page size is a multiple of 16), then all 16 groups' key loads are issued
-// before the first MFMA (32 KB in flight per wave, two waves per SIMD).  The ReLU, the head weights and the reduction over heads stay in
-// registers; the head reduction crosses the four 16-lane groups with two
-// permlane swaps.  The scan is HBM-bound (128 FLOP/byte).
+// chunk of 256 entries; each wave owns 64 consecutive entries = 4 groups of
+// 16.  Per group a wave runs one v_mfma 16x16x128 FP8 per 16 index heads:
+// A = the query's index heads (rows) x 128 dims; B = 16 entry keys x 128
+// dims, loaded straight from memory into the operand registers (each key
+// byte is used once, so no LDS staging).  The workgroup reads the query
+// operand once (one tile of 16 heads per wave) and shares it through LDS.
+// The pages of the wave's groups come from one vector load (lane u fetches
+// group u's page id; a group of 16 never straddles a page because the page
+// size is a multiple of 16), then all of the wave's key loads are issued
+// before the first MFMA.  Short workgroups at four waves per SIMD keep 8 KB
+// in flight per wave and let the hardware rebalance ragged rows as
+// workgroups finish.  The ReLU, the head weights and the reduction over
+// heads stay in registers; the head reduction crosses the four 16-lane
+// groups with two permlane swaps.  The scan is HBM-bound (128 FLOP/byte).
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -27,16 +30,21 @@ namespace csa {
 
 namespace {
 
-constexpr int kIdxWaves = 4;
-
 // max(x, 0) as one v_med3_f32 (fmaxf on an MFMA result costs a canonicalising
 // v_max first)
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
-constexpr int kIdxGroups = 16;                       // groups of 16 entries per wave
-constexpr int kIdxWaveEntries = 16 * kIdxGroups;     // 256
-constexpr int kIdxChunk = kIdxWaves * kIdxWaveEntries;
 
-__global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexParams p) {
+// kWaves waves of kGroups groups of 16 entries: a workgroup scores
+// kWaves * kGroups * 16 consecutive entries of one query row.  kQLds: the
+// workgroup reads the query operand from memory once and hands it to its
+// waves through LDS (else every wave loads its own copy).
+template <int kWaves, int kGroups, int kOcc, bool kQLds>
+__global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexParams p) {
+  static_assert(!kQLds || kWaves >= 4, "four waves fill the shared query operand");
+  static_assert(kGroups <= 64, "one page-id lane per group");
+  constexpr int kWaveEntries = 16 * kGroups;
+  constexpr int kChunk = kWaves * kWaveEntries;
+  __shared__ v8i qs[kQLds ? 4 * 64 : 1];
   const int t = blockIdx.x / p.n_chunks;
   const int chunk = blockIdx.x - t * p.n_chunks;
   const int lane = threadIdx.x & 63;
@@ -50,17 +58,26 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   // is waited for.  Query operand: 4 tiles of 16 index heads; lane holds
   // head 16 ht + r, dims [32 g, 32 g + 32).  Weights of output rows
   // (heads 16 ht + 4 g + i), read as one 16-byte load per tile.
-  v8i qa[4];
-  v4f wv[4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
+  auto load_q = [&](int ht) -> v8i {
     const int h = 16 * ht + r;
-    qa[ht] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    v8i a = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
     if (h < p.H_I && dim_ok) {
       const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
       const v4i lo = ld16(src), hi = ld16(src + 16);
-      qa[ht] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+    return a;
+  };
+  v8i qa[4];
+  if (kQLds) {
+    if (wave < 4) qa[0] = load_q(wave);   // wave w < 4 fetches tile w
+  } else {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) qa[ht] = load_q(ht);
+  }
+  v4f wv[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
     const int h0 = 16 * ht + 4 * g;
     if (h0 + 3 < p.H_I && (p.H_I & 3) == 0 && ((uintptr_t)p.w & 15) == 0) {
       wv[ht] = *reinterpret_cast<const v4f*>(p.w + (size_t)t * p.H_I + h0);
@@ -71,12 +88,13 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   }
   const int seq = p.q_seq[t];
   const int pos = p.q_pos[t];
-  const int e_begin = chunk * kIdxChunk + wave * kIdxWaveEntries;
+  const int e_begin = chunk * kChunk + wave * kWaveEntries;
   const bool seq_ok = seq >= 0 && seq < p.B;
-  // Page of every group (lane u < 16 fetches group u's page id); a group of
-  // 16 never straddles a page because the page size is a multiple of 16.
+  // Page of every group (lane u < kGroups fetches group u's page id); a
+  // group of 16 never straddles a page because the page size is a multiple
+  // of 16.
   int my_page = -1;
-  if (seq_ok && lane < kIdxGroups) {
+  if (seq_ok && lane < kGroups) {
     const int pi = (e_begin + 16 * lane) / p.page_size;
     if (pi < p.max_pages) my_page = p.page_table[(size_t)seq * p.max_pages + pi];
   }
@@ -84,16 +102,18 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   if (seq_ok && pos >= 0) nv = min(pos / p.ratio_m, p.n_comp[seq]);
   nv = max(0, min(nv, (int)min<int64_t>(p.ld, 0x7fffffff)));
   if (chunk == 0 && threadIdx.x == 0) p.n_visible[t] = nv;
-  if (e_begin >= nv) return;
-  const int e_end = min(nv, e_begin + kIdxWaveEntries);
+  // a workgroup whose first entry is past the visible range has nothing to
+  // do (uniform, so the LDS hand-over below is never split)
+  if (chunk * kChunk >= nv) return;
+  const int e_end = min(nv, e_begin + kWaveEntries);
 
   // ---- all key loads back to back.  Group u covers entries
   // e_begin + 16 u + (0..15); lane (g, r) loads entry r's dims [32 g, 32 g + 32).
   int poff = e_begin % p.page_size;        // uniform: offset of group u in its page
-  v8i kb[kIdxGroups];
+  v8i kb[kGroups];
   uint32_t ok_mask = 0;                    // uniform: group has a valid page
 #pragma unroll
-  for (int u = 0; u < kIdxGroups; ++u) {
+  for (int u = 0; u < kGroups; ++u) {
     const int e0 = e_begin + 16 * u;
     const int page = __builtin_amdgcn_readlane(my_page, u);
     const bool ok = e0 < e_end && page >= 0 && page < p.num_pages;
@@ -108,8 +128,16 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
     poff += 16;
     if (poff >= p.page_size) poff -= p.page_size;
   }
+  if (kQLds) {
+    // the query tile arrived with the page ids, ahead of the keys
+    if (wave < 4) qs[wave * 64 + lane] = qa[0];
+    lds_barrier();
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) qa[ht] = qs[ht * 64 + lane];
+  }
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) wv[ht] *= p.qk_scale;
+  if (e_begin >= nv) return;
 
   // ---- software pipeline: the MFMAs of group u + 1 go out before the
   // weighted ReLU of group u; the head sum runs as four independent chains
@@ -122,8 +150,8 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void index_scores_kernel(IndexPa
   v4f acc[2][4];
   mfmas(kb[0], acc[0]);
 #pragma unroll
-  for (int u = 0; u < kIdxGroups; ++u) {
-    if (u + 1 < kIdxGroups) mfmas(kb[u + 1], acc[(u + 1) & 1]);
+  for (int u = 0; u < kGroups; ++u) {
+    if (u + 1 < kGroups) mfmas(kb[u + 1], acc[(u + 1) & 1]);
     float pp[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -300,6 +328,18 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   }
 }
 
+template <int kWaves, int kGroups, int kOcc, bool kQLds>
+hipError_t launch_decode(IndexParams p, int64_t span, hipStream_t stream) {
+  constexpr int kChunk = kWaves * kGroups * 16;
+  p.chunk = kChunk;
+  p.n_chunks = (int)std::max<int64_t>(1, (span + kChunk - 1) / kChunk);
+  const int64_t blocks = (int64_t)p.T * p.n_chunks;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((index_scores_kernel<kWaves, kGroups, kOcc, kQLds>), dim3((unsigned)blocks), dim3(64 * kWaves), 0,
+                     stream, p);
+  return hipPeekAtLastError();
+}
+
 }  // namespace
 
 hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
@@ -317,12 +357,7 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
                        n_split);
     return hipPeekAtLastError();
   }
-  p.chunk = kIdxChunk;
-  p.n_chunks = (int)std::max<int64_t>(1, (span + kIdxChunk - 1) / kIdxChunk);
-  const int64_t blocks = (int64_t)p.T * p.n_chunks;
-  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(index_scores_kernel, dim3((unsigned)blocks), dim3(64 * kIdxWaves), 0, stream, p);
-  return hipPeekAtLastError();
+  return launch_decode<4,4,4,true>(p, span, stream);
 }
 
 }  // namespace csa

@@ -118,6 +118,29 @@ def test_tiny_dims_64_head_workgroups():
     check_full(ci.generate(spec, seed=112), queries=[0, 5, 130, 255, 259])
 
 
+def test_decode_1100_sequences_tiny_dims():
+    # a wide decode batch: many short ragged rows, most indexer workgroups
+    # past their row's visible range
+    say("case decode 1100 sequences (tiny dims)")
+    rng = np.random.default_rng(113)
+    lens = [int(x) * 4 for x in rng.integers(40, 160, size=1100)]
+    spec = ci.Spec(name="tiny_decode_1100", kind="decode", ctx_lens=lens, H=8, D_nope=48, D_rope=16, H_I=4, D_I=32,
+                   k=16, W=32, page_size=16, shuffle_pages=True)
+    check_full(ci.generate(spec, seed=113), queries=[0, 1, 517, 1023, 1024, 1099])
+
+
+def test_decode_fewer_stored_entries_than_position_allows():
+    # n_comp below pos / m: the visible range ends at the stored entries,
+    # not at the position's bound
+    say("case decode with unstored compressed entries")
+    wl = ci.generate(ci.small_spec(ctx_lens=[4096, 2052, 3000, 1500], shuffle_pages=True), seed=114)
+    n_comp = wl.n_comp.copy()
+    n_comp[0] = 700
+    n_comp[2] = 3
+    n_comp[3] = 0
+    check_full(dataclasses.replace(wl, n_comp=n_comp))
+
+
 def test_ring_permutation_invariance_gpu():
     say("case ring permutation")
     wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1800]), seed=105)
