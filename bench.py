@@ -8,10 +8,15 @@ latent, indexer 64 x 128, top-k 512, window 128).
 
 Output: one JSON line with the throughput, a roofline object for the
 dominant kernel (algorithmic bytes or FLOPs per launch / the kernel's
-average duration measured with HIP events on its stream over the timed
-region), and the FP64 CPU oracle timed on a bounded sample of the same
-workload.  Inputs are rotated over several device copies so that every step
-reads HBM, not the 256 MB Infinity Cache.
+average duration measured with HIP events on its stream), and the FP64 CPU
+oracle timed on a bounded sample of the same workload.  Inputs are rotated
+over several device copies so that every step reads HBM, not the 256 MB
+Infinity Cache.
+
+Two timed regions: the throughput comes from K whole steps back to back with
+no event between the kernels (an event record between two kernels adds a
+few microseconds of idle GPU); the per-kernel durations come from a second
+region that launches each stage K times back to back between two events.
 """
 from __future__ import annotations
 
@@ -231,20 +236,34 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    # Timed region 1, the headline: K whole steps back to back, nothing else
+    # on the stream (an event record between two kernels adds a gap of a few
+    # microseconds on this GPU, so per-kernel events stay out of this loop).
+    e_begin = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_begin.record(stream)
     for i in range(K):
-        p = paths[i % copies]
-        e = evs[i]
-        for j in range(len(stages)):
-            e[j].record(stream)
-            p.run_stage(j, st)
-        e[-1].record(stream)
+        paths[i % copies].run(st)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_stage = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K for j in range(len(stages))]
-    gpu_step = sum(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K)) / K
+    gpu_step = e_begin.elapsed_time(e_end) / K
+    # Timed region 2, per-kernel durations: each stage launched K times back
+    # to back (over the same rotating input copies, whose earlier stages ran
+    # above) between two events on the launch stream.
+    per_stage = []
+    for j in range(len(stages)):
+        ea = torch.cuda.Event(enable_timing=True)
+        eb = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record(stream)
+        for i in range(K):
+            paths[i % copies].run_stage(j, st)
+        eb.record(stream)
+        torch.cuda.synchronize()
+        per_stage.append(ea.elapsed_time(eb) / K)
     ms_per_step = wall * 1e3 / K
     n_items = wl.T
     value = n_items / (ms_per_step * 1e-3)
