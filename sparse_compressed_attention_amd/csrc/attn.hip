@@ -79,20 +79,30 @@ struct Cfg {
   static_assert(REM <= 64, "remainder block must fit one combined hi|lo MFMA");
 };
 
-// What dim half DH of a head tile owns.
-template <int DN, int DR, int DH>
-struct Half {
+// What dim part DP of ND (2 or 4) of a head tile owns: nope blocks
+// [BB, BE) (128 dims each; block NFB is the combined hi|lo block of the last
+// REM <= 64 nope dims) and, in the last part, the rope dims.  Two parts split
+// the nope blocks in half; four parts take one nope block each.
+template <int DN, int DR, int ND, int DP>
+struct Part {
   using C = Cfg<DN, DR>;
-  static constexpr int FB = DH == 0 ? (C::B0 < C::NFB ? C::B0 : C::NFB) : (C::NFB > C::B0 ? C::NFB - C::B0 : 0);
-  static constexpr int FB0 = DH == 0 ? 0 : C::B0;           // first full block
-  static constexpr bool COMB = C::REM > 0 && ((C::NFB < C::B0) == (DH == 0));
-  static constexpr int NR = DH == 1 ? (DR + 31) / 32 : 0;    // rope k-steps of QK
-  static constexpr int PT0 = DH == 0 ? 0 : C::N0 / 16;       // first nope dim tile of PV
-  static constexpr int NPT = DH == 0 ? C::N0 / 16 : C::CHN - C::N0 / 16;
-  static constexpr int NRT = DH == 1 ? DR / 16 : 0;          // rope dim tiles of PV
-  static constexpr int NO = NPT + NRT;                       // O accumulators
+  static_assert(ND == 2 || ND == 4, "two or four dim parts");
+  static_assert(ND == 2 || C::NBLK == ND, "four parts take one nope block each");
+  static constexpr bool LAST = DP == ND - 1;
+  static constexpr int BB = ND == 2 ? (DP == 0 ? 0 : C::B0) : DP;
+  static constexpr int BE = ND == 2 ? (DP == 0 ? C::B0 : C::NBLK) : DP + 1;
+  static constexpr int FB = (BE < C::NFB ? BE : C::NFB) - (BB < C::NFB ? BB : C::NFB);   // full blocks
+  static constexpr int FB0 = BB;                                         // first full block
+  static constexpr bool COMB = C::REM > 0 && BB <= C::NFB && C::NFB < BE;
+  static constexpr int NR = LAST ? (DR + 31) / 32 : 0;                   // rope k-steps of QK
+  static constexpr int D0 = 128 * BB < DN ? 128 * BB : DN;               // nope dims [D0, D1)
+  static constexpr int D1 = 128 * BE < DN ? 128 * BE : DN;
+  static constexpr int PT0 = D0 / 16;                                    // first nope dim tile of PV
+  static constexpr int NPT = (D1 - D0) / 16;
+  static constexpr int NRT = LAST ? DR / 16 : 0;                         // rope dim tiles of PV
+  static constexpr int NO = NPT + NRT;                                   // O accumulators
   static constexpr int NQB = FB + (COMB ? 1 : 0);
-  static_assert(NO >= 1, "every dim half owns output dims");
+  static_assert(NO >= 1, "every dim part owns output dims");
 };
 
 // key (0..31) held by byte e (0..7) of a lane in 16-lane group g: the keys
@@ -140,22 +150,25 @@ __device__ __forceinline__ int page_div(int n, const AttnParams& p) {
   return (int)(((uint64_t)(uint32_t)n * p.ps_magic) >> p.ps_shift);
 }
 
+// Source of the tile rows of masked keys.
+__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[512] = {};
+
 struct Block {
   int t, hg, split, seq;
   int pos, nc;
   int n_sel, sel_end, kv0, nkeys;   // slots: [0, n_sel) selected, [sel_end, sel_end + W) window
 };
 
-template <int DN, int DR, int DH, int HT>
+template <int DN, int DR, int DP, int HT, int ND>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, uint8_t* xs0, int32_t* desc,
                                           v4f* sx, int wave) {
   using C = Cfg<DN, DR>;
-  using HF = Half<DN, DR, DH>;
+  using HF = Part<DN, DR, ND, DP>;
   constexpr int D = DN + DR;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int r = lane & 15;
-  constexpr int kWaves = 2 * HT;              // waves (head tile, dim half)
+  constexpr int kWaves = ND * HT;             // waves (head tile, dim part): wave = DP * HT + ht
   constexpr int kThreads = 64 * kWaves;
   const int ht = wave % HT;
   const int h = bk.hg * (16 * HT) + ht * 16 + r;
@@ -253,9 +266,9 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 
   // ---- tile DMA: wave w fills the quads of keys [16 w, 16 w + 16); lane l
   // copies 16 bytes of chunk 4 q + l / 16 of key dkey into LDS byte
-  // (q * 4 + w) * 1024 + 16 l.  Masked keys copy a dummy row (row 0) so that
-  // every wave issues the same number of DMAs per tile; those rows are
-  // cleared in LDS before use.
+  // (q * 4 + w) * 1024 + 16 l.  Masked keys copy a row of zeros, so that
+  // every wave issues the same number of DMAs per tile and those keys add
+  // nothing to S or O.
   const int dcc = lane >> 4;
   const int drg = wave & 3;                   // row group (16 keys) this wave copies
   const int dq0 = wave >> 2;                  // first quad; then every kQStep-th
@@ -265,8 +278,8 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   auto prep_tile = [&](int tile) {
     const int s = tile * kAttnTile + dkey;
     const int d = s < nkeys ? desc[s] : -1;
-    const uint8_t* nsrc = p.lat_nope;
-    const uint8_t* rsrc = reinterpret_cast<const uint8_t*>(p.lat_rope);
+    const uint8_t* nsrc = kZeroRow;
+    const uint8_t* rsrc = kZeroRow;
     if (d >= 0) {
       const size_t row = (size_t)(d & ~kSwaFlag);
       if (d & kSwaFlag) {
@@ -392,8 +405,240 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     rp_off[u][1] = rb_ * 256 + key_part(32 * u + kappa(g, 4 + (r >> 2)), rb_) + 8 * (r & 1);
   }
   v4f* sx_own = sx + (size_t)wave * 4 * 64 + lane;
-  const v4f* sx_oth = sx + (size_t)((wave + HT) % kWaves) * 4 * 64 + lane;
+  const v4f* sx_tile = sx + (size_t)ht * 4 * 64 + lane;   // part dp of this head tile at + dp HT 4 64
 
+  // ---- one tile's steps
+  v4f acc[4], racc[4];
+  // QK: partial scores over this half's dims of the tile in buffer xq
+  auto qk = [&](const uint8_t* xq) {
+      // -- partial scores over this half's dims: four 16-key subtiles; the
+      //    operands of the next step are read before the MFMAs of this one
+  #pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        acc[st] = (v4f){0.f, 0.f, 0.f, 0.f};
+        racc[st] = acc[st];
+      }
+      if (tile_ok) {
+        constexpr int NSTEP = HF::FB + (HF::COMB ? 1 : 0);
+        auto read_step = [&](int step, v8i (&x)[4]) {
+  #pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            if (step < HF::FB) {
+              // chunks 8 (FB0 + step) + 2 g and + 1 (even, odd)
+              const uint8_t* base = xq + (HF::FB0 + step) * 8192 + qk_g;
+              const v4i lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
+              const v4i hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
+              x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+              // chunks 8 NFB + 2 (g & 1) and + 1
+              const uint8_t* base = xq + C::NFB * 8192 + 512 * (g & 1);
+              v4i lo = (v4i){0, 0, 0, 0}, hi = lo;
+              if (32 * (g & 1) < C::REM) lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
+              if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
+              x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+          }
+        };
+        v8i x[2][4];
+        v4i y[HF::NR > 0 ? HF::NR : 1][4];
+        if (NSTEP > 0) read_step(0, x[0]);
+  #pragma unroll
+        for (int rr = 0; rr < HF::NR; ++rr) {
+          // rope chunk CHNP + 4 rr + g (parity g & 1)
+          const uint8_t* base = xq + ((C::CHNP / 4 + rr) * 16 + g) * 256;
+  #pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            y[rr][st] = (v4i){0, 0, 0, 0};
+            if (32 * rr + 8 * g < DR) y[rr][st] = *reinterpret_cast<const v4i*>(base + qk_off[st][g & 1]);
+          }
+        }
+  #pragma unroll
+        for (int step = 0; step < NSTEP; ++step) {
+          if (step + 1 < NSTEP) read_step(step + 1, x[(step + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (step < HF::FB) {
+  #pragma unroll
+            for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qhi[step], acc[st]);
+  #pragma unroll
+            for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qlo[step], acc[st]);
+          } else {
+  #pragma unroll
+            for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qcomb, acc[st]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  #pragma unroll
+        for (int rr = 0; rr < HF::NR; ++rr)
+  #pragma unroll
+          for (int st = 0; st < 4; ++st)
+            racc[st] = mfma_bf16_32(__builtin_bit_cast(v8bf, y[rr][st]), qr[rr], racc[st]);
+      }
+  };
+  // valid keys of tile `it` (the same in every wave): bit k = key k.  Masked
+  // keys were copied from a zero row, so they add nothing to S or O; dim
+  // half 0 gives them -inf in the exchanged score.
+  auto tile_mask = [&](int it) -> uint64_t {
+    const int sk = it * kAttnTile + lane;
+    const int dk = sk < nkeys ? desc[sk] : -1;
+    return __ballot(dk >= 0);
+  };
+  // own partial (scaled) of the exchanged score
+  auto own_part = [&](uint64_t vmask, bool tile_swa, v4f (&part)[4]) {
+    const bool full = vmask == ~0ull;
+      // -- own partial (scaled), exchanged with the other dim half of the head
+      //    tile.  Half 0 also subtracts the running max (so the sum S' is the
+      //    exp2 argument) and carries -inf for masked keys (lane keys
+      //    16 st + 4 g + i).
+      const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+      const float ks = tile_swa ? cqs : cql;
+  #pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (DP == 0) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) part[st][i] = __builtin_fmaf(acc[st][i], ks, -msub);
+        } else {
+          part[st] = acc[st] * ks + racc[st] * cr;
+        }
+      }
+      if (DP == 0 && !full) {
+  #pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const uint32_t vw = st < 2 ? (uint32_t)vmask : (uint32_t)(vmask >> 32);
+          const uint32_t bits = vw >> (16 * (st & 1) + 4 * g);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((bits >> i) & 1u)) part[st][i] = -__builtin_inff();
+        }
+      }
+  };
+  // online softmax and PV of tile `it` (tot: the exchanged score, summed over
+  // the dim parts in the same order in every part)
+  auto soft_pv = [&](int it, const v4f (&tot)[4], const uint8_t* xb, bool tile_swa) {
+    const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // as subtracted in own_part
+      if (tile_ok) {
+        // -- online softmax (lane: head h, keys 16 st + 4 g + i); sv = S - msub
+        float sv[16];
+        float tmax = -__builtin_inff();
+  #pragma unroll
+        for (int st = 0; st < 4; ++st) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[4 * st + i] = tot[st][i];
+            tmax = fmaxf(tmax, tot[st][i]);
+          }
+        }
+        tmax = max_over_groups(tmax);
+        const bool m_inf = m_run == -__builtin_inff();
+        const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
+        float pr[16];
+        float psum = 0.0f;
+        if (__ballot(grow)) {
+          // raise the running max to the tile max on the lanes that grew
+          const float delta = grow ? tmax : 0.0f;
+          const float alpha = grow ? (m_inf ? 0.0f : __builtin_amdgcn_exp2f(-tmax)) : 1.0f;
+          if (grow) m_run = msub + tmax;
+          l_run *= alpha;
+          if (it > 0) {
+  #pragma unroll
+            for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
+          }
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            pr[e] = __builtin_amdgcn_exp2f(sv[e] - delta);
+            psum += pr[e];
+          }
+        } else {
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            pr[e] = __builtin_amdgcn_exp2f(sv[e]);   // exp2(-inf) = 0 for masked keys
+            psum += pr[e];
+          }
+        }
+        l_run += psum;
+
+        // -- P operand for nope: bytes [hi of the lane's 16 keys | lo of them]
+        //    of p x key-scale ratio x 2^(8 - tau); lo = the rounding residual
+        const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
+        v8i pb;
+  #pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float x0 = pr[4 * st] * kq, x1 = pr[4 * st + 1] * kq;
+          const float x2 = pr[4 * st + 2] * kq, x3 = pr[4 * st + 3] * kq;
+          const int w = pack4_fp8(x0, x1, x2, x3);
+          const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+          const v2f b23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+          pb[st] = w;
+          pb[4 + st] = pack4_fp8(x0 - b01[0], x1 - b01[1], x2 - b23[0], x3 - b23[1]);
+        }
+
+        // -- PV: O^T[dims x heads] += X^T[dims x K] P^T[K x heads]; A = the
+        //    two 8-key transpose reads, used for the hi and the lo half of K.
+        //    Reads of the next batch go out before the MFMAs of this one.
+        {
+          constexpr int PB = 4;   // dim tiles per batch
+          constexpr int NB = (HF::NPT + PB - 1) / PB;
+          v2i ra[2][PB], rb[2][PB];
+          auto read_batch = [&](int bt, v2i (&a)[PB], v2i (&b)[PB]) {
+  #pragma unroll
+            for (int j = 0; j < PB; ++j) {
+              const int dt = bt * PB + j;
+              if (dt < HF::NPT) {
+                const int c = HF::PT0 + dt;
+                const uint8_t* cb = xb + chunk_base(c);
+                a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[0][c & 1]));
+                b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[1][c & 1]));
+              }
+            }
+          };
+          if (NB > 0) read_batch(0, ra[0], rb[0]);
+  #pragma unroll
+          for (int bt = 0; bt < NB; ++bt) {
+            if (bt + 1 < NB) read_batch(bt + 1, ra[(bt + 1) & 1], rb[(bt + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+            for (int j = 0; j < PB; ++j) {
+              const int dt = bt * PB + j;
+              if (dt < HF::NPT) {
+                const v2i a0 = ra[bt & 1][j], a1 = rb[bt & 1][j];
+                const v8i a = (v8i){a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};
+                O[dt] = mfma_f8_128(a, pb, O[dt]);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (HF::NRT > 0) {
+          // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7); rope dim tile
+          // j = chunks CHNP + 2 j (+1)
+          v4i pbf[2];
+  #pragma unroll
+          for (int u = 0; u < 2; ++u)
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) pbf[u][e] = (int)pack2_bf16(pr[8 * u + 2 * e], pr[8 * u + 2 * e + 1]);
+          v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
+  #pragma unroll
+          for (int j = 0; j < HF::NRT; ++j) {
+            const uint8_t* cb = xb + ((C::CHNP / 4 + (j >> 1)) * 16 + 2 * (j & 1)) * 256;
+  #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const v2i lo = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][0])));
+              const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][1])));
+              ya[j][u] = (v4i){lo[0], lo[1], hi[0], hi[1]};
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int u = 0; u < 2; ++u)
+  #pragma unroll
+            for (int j = 0; j < HF::NRT; ++j)
+              O[HF::NPT + j] = mfma_bf16_32(__builtin_bit_cast(v8bf, ya[j][u]), __builtin_bit_cast(v8bf, pbf[u]),
+                                            O[HF::NPT + j]);
+        }
+      }
+  };
+
+  // ---- the tiles: a barrier for each tile's arrival and one for the score
+  // exchange; the other waves on the SIMD hide each other's latencies
   int buf = 0;
   for (int it = 0; it < n_tiles; ++it, buf = (buf + 1 == kNBuf) ? 0 : buf + 1) {
     // tile `it` landed in LDS (this wave's DMAs), then everyone's (barrier);
@@ -408,245 +653,27 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
       prep_tile(it + 2);
       issue_quads(nbuf, 0);
     }
-    uint8_t* xb = xs0 + buf * C::TILE_BYTES;
-
-    // -- valid keys of the tile (the same in every wave): bit k = key k.
-    //    Rows of masked keys are cleared, so they add nothing to S or O.
-    const int sk = it * kAttnTile + lane;
-    const int dk = sk < nkeys ? desc[sk] : -1;
-    const uint64_t vmask = __ballot(dk >= 0);
-    const bool full = vmask == ~0ull;
-    if (!full) {
-      if (!((vmask >> dkey) & 1ull)) {
-#pragma unroll
-        for (int q = 0; q < C::NQ; ++q)
-          if (q % kQStep == dq0) *reinterpret_cast<v4i*>(xb + (q * 4 + drg) * 1024 + 16 * lane) = (v4i){0, 0, 0, 0};
-      }
-      lds_barrier();
-    }
-    // a tile holds only compressed entries or only window rows
+    const uint8_t* xb = xs0 + buf * C::TILE_BYTES;
+    const uint64_t vmask = tile_mask(it);
     const bool tile_swa = kv0 + it * kAttnTile >= sel_end;
-
-    // -- partial scores over this half's dims: four 16-key subtiles; the
-    //    operands of the next step are read before the MFMAs of this one
-    v4f acc[4], racc[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      acc[st] = (v4f){0.f, 0.f, 0.f, 0.f};
-      racc[st] = acc[st];
-    }
-    if (tile_ok) {
-      constexpr int NSTEP = HF::FB + (HF::COMB ? 1 : 0);
-      auto read_step = [&](int step, v8i (&x)[4]) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          if (step < HF::FB) {
-            // chunks 8 (FB0 + step) + 2 g and + 1 (even, odd)
-            const uint8_t* base = xb + (HF::FB0 + step) * 8192 + qk_g;
-            const v4i lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
-            const v4i hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
-            x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          } else {
-            // chunks 8 NFB + 2 (g & 1) and + 1
-            const uint8_t* base = xb + C::NFB * 8192 + 512 * (g & 1);
-            v4i lo = (v4i){0, 0, 0, 0}, hi = lo;
-            if (32 * (g & 1) < C::REM) lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
-            if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
-            x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-        }
-      };
-      v8i x[2][4];
-      v4i y[HF::NR > 0 ? HF::NR : 1][4];
-      if (NSTEP > 0) read_step(0, x[0]);
-#pragma unroll
-      for (int rr = 0; rr < HF::NR; ++rr) {
-        // rope chunk CHNP + 4 rr + g (parity g & 1)
-        const uint8_t* base = xb + ((C::CHNP / 4 + rr) * 16 + g) * 256;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          y[rr][st] = (v4i){0, 0, 0, 0};
-          if (32 * rr + 8 * g < DR) y[rr][st] = *reinterpret_cast<const v4i*>(base + qk_off[st][g & 1]);
-        }
-      }
-#pragma unroll
-      for (int step = 0; step < NSTEP; ++step) {
-        if (step + 1 < NSTEP) read_step(step + 1, x[(step + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (step < HF::FB) {
-#pragma unroll
-          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qhi[step], acc[st]);
-#pragma unroll
-          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qlo[step], acc[st]);
-        } else {
-#pragma unroll
-          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qcomb, acc[st]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int rr = 0; rr < HF::NR; ++rr)
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          racc[st] = mfma_bf16_32(__builtin_bit_cast(v8bf, y[rr][st]), qr[rr], racc[st]);
-    }
-
-    // -- own partial (scaled), exchanged with the other dim half of the head
-    //    tile.  Half 0 also subtracts the running max (so the sum S' is the
-    //    exp2 argument) and carries -inf for masked keys (lane keys
-    //    16 st + 4 g + i).
-    const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
-    const float ks = tile_swa ? cqs : cql;
+    qk(xb);
     v4f part[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if (DH == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[st][i] = __builtin_fmaf(acc[st][i], ks, -msub);
-      } else {
-        part[st] = acc[st] * ks + racc[st] * cr;
-      }
-    }
-    if (DH == 0 && !full) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const uint32_t vw = st < 2 ? (uint32_t)vmask : (uint32_t)(vmask >> 32);
-        const uint32_t bits = vw >> (16 * (st & 1) + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (!((bits >> i) & 1u)) part[st][i] = -__builtin_inff();
-      }
-    }
+    own_part(vmask, tile_swa, part);
 #pragma unroll
     for (int st = 0; st < 4; ++st) sx_own[st * 64] = part[st];
     if (refill) issue_quads(nbuf, 1);
     lds_barrier();
-    v4f oth[4];
+    v4f pp[ND][4];   // the parts' partials: own from registers, the others from LDS
 #pragma unroll
-    for (int st = 0; st < 4; ++st) oth[st] = sx_oth[st * 64];
+    for (int dp = 0; dp < ND; ++dp)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) pp[dp][st] = dp == DP ? part[st] : sx_tile[(dp * HT * 4 + st) * 64];
+    v4f tot[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      tot[st] = ND == 2 ? pp[0][st] + pp[1][st] : (pp[0][st] + pp[1][st]) + (pp[ND - 2][st] + pp[ND - 1][st]);
     __builtin_amdgcn_sched_barrier(0);
-
-    if (tile_ok) {
-      // -- online softmax (lane: head h, keys 16 st + 4 g + i); sv = S - msub
-      float sv[16];
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const v4f tot = DH == 0 ? part[st] + oth[st] : oth[st] + part[st];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[4 * st + i] = tot[i];
-          tmax = fmaxf(tmax, tot[i]);
-        }
-      }
-      tmax = max_over_groups(tmax);
-      const bool m_inf = m_run == -__builtin_inff();
-      const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
-      float pr[16];
-      float psum = 0.0f;
-      if (__ballot(grow)) {
-        // raise the running max to the tile max on the lanes that grew
-        const float delta = grow ? tmax : 0.0f;
-        const float alpha = grow ? (m_inf ? 0.0f : __builtin_amdgcn_exp2f(-tmax)) : 1.0f;
-        if (grow) m_run = msub + tmax;
-        l_run *= alpha;
-        if (it > 0) {
-#pragma unroll
-          for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          pr[e] = __builtin_amdgcn_exp2f(sv[e] - delta);
-          psum += pr[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          pr[e] = __builtin_amdgcn_exp2f(sv[e]);   // exp2(-inf) = 0 for masked keys
-          psum += pr[e];
-        }
-      }
-      l_run += psum;
-
-      // -- P operand for nope: bytes [hi of the lane's 16 keys | lo of them]
-      //    of p x key-scale ratio x 2^(8 - tau); lo = the rounding residual
-      const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
-      v8i pb;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float x0 = pr[4 * st] * kq, x1 = pr[4 * st + 1] * kq;
-        const float x2 = pr[4 * st + 2] * kq, x3 = pr[4 * st + 3] * kq;
-        const int w = pack4_fp8(x0, x1, x2, x3);
-        const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-        const v2f b23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-        pb[st] = w;
-        pb[4 + st] = pack4_fp8(x0 - b01[0], x1 - b01[1], x2 - b23[0], x3 - b23[1]);
-      }
-
-      // -- PV: O^T[dims x heads] += X^T[dims x K] P^T[K x heads]; A = the
-      //    two 8-key transpose reads, used for the hi and the lo half of K.
-      //    Reads of the next batch go out before the MFMAs of this one.
-      {
-        constexpr int PB = 4;   // dim tiles per batch
-        constexpr int NB = (HF::NPT + PB - 1) / PB;
-        v2i ra[2][PB], rb[2][PB];
-        auto read_batch = [&](int bt, v2i (&a)[PB], v2i (&b)[PB]) {
-#pragma unroll
-          for (int j = 0; j < PB; ++j) {
-            const int dt = bt * PB + j;
-            if (dt < HF::NPT) {
-              const int c = HF::PT0 + dt;
-              const uint8_t* cb = xb + chunk_base(c);
-              a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[0][c & 1]));
-              b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[1][c & 1]));
-            }
-          }
-        };
-        if (NB > 0) read_batch(0, ra[0], rb[0]);
-#pragma unroll
-        for (int bt = 0; bt < NB; ++bt) {
-          if (bt + 1 < NB) read_batch(bt + 1, ra[(bt + 1) & 1], rb[(bt + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int j = 0; j < PB; ++j) {
-            const int dt = bt * PB + j;
-            if (dt < HF::NPT) {
-              const v2i a0 = ra[bt & 1][j], a1 = rb[bt & 1][j];
-              const v8i a = (v8i){a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};
-              O[dt] = mfma_f8_128(a, pb, O[dt]);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      if (HF::NRT > 0) {
-        // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7); rope dim tile
-        // j = chunks CHNP + 2 j (+1)
-        v4i pbf[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pbf[u][e] = (int)pack2_bf16(pr[8 * u + 2 * e], pr[8 * u + 2 * e + 1]);
-        v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
-#pragma unroll
-        for (int j = 0; j < HF::NRT; ++j) {
-          const uint8_t* cb = xb + ((C::CHNP / 4 + (j >> 1)) * 16 + 2 * (j & 1)) * 256;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const v2i lo = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][0])));
-            const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][1])));
-            ya[j][u] = (v4i){lo[0], lo[1], hi[0], hi[1]};
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int j = 0; j < HF::NRT; ++j)
-            O[HF::NPT + j] = mfma_bf16_32(__builtin_bit_cast(v8bf, ya[j][u]), __builtin_bit_cast(v8bf, pbf[u]),
-                                          O[HF::NPT + j]);
-      }
-    }
+    soft_pv(it, tot, xb, tile_swa);
     if (refill) issue_quads(nbuf, 2);
   }
   if (!tile_ok) return;
@@ -670,7 +697,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         *reinterpret_cast<v4f*>(p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + kPartPad) + dim) = v;
       }
     }
-    if (DH == 0 && g == 0) {
+    if (DP == 0 && g == 0) {
       if (final_out) {
         if (p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
       } else {
@@ -682,16 +709,18 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   }
 }
 
-// HT = 16-head tiles per workgroup: 2 (4 waves, one per SIMD) when there are
-// few queries, 4 (8 waves, two per SIMD, each tile shared by 64 heads) when
-// there are enough (query, head group) pairs to fill the GPU without
-// splitting key ranges.
-template <int DN, int DR, int HT>
-__global__ __launch_bounds__(128 * HT, 1) void attn_kernel(AttnParams p) {
+// HT = 16-head tiles per workgroup, ND = dim parts per head tile; one wave
+// per (tile, part), so ND * HT waves.  Few queries: HT = 2 with ND = 4 (eight
+// waves on 32 heads, two per SIMD, so that one wave's softmax runs while the
+// other's MFMAs do).  Enough (query, head group) pairs to fill the GPU
+// without splitting key ranges: HT = 4 with ND = 2 (each tile shared by 64
+// heads, again two waves per SIMD).
+template <int DN, int DR, int HT, int ND>
+__global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   using C = Cfg<DN, DR>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf * C::TILE_BYTES];
   __shared__ int32_t desc[kAttnMaxSlots];
-  __shared__ v4f sx[2 * HT * 4 * 64];   // partial score tiles, [wave][subtile][lane]
+  __shared__ v4f sx[ND * HT * 4 * 64];   // partial score tiles, [wave][subtile][lane]
 
   // ---- which (query, head group, split).  Workgroups go to the 8 XCDs
   // round-robin by id.  With 8 or more queries, queries are spread over the
@@ -733,11 +762,22 @@ __global__ __launch_bounds__(128 * HT, 1) void attn_kernel(AttnParams p) {
   bk.nkeys = max(0, min(n_slots, bk.kv0 + p.per_split) - bk.kv0);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __builtin_assume(wave >= 0 && wave < 2 * HT);
-  if (wave >= HT)
-    attn_wave<DN, DR, 1, HT>(p, bk, xs, desc, sx, wave);
-  else
-    attn_wave<DN, DR, 0, HT>(p, bk, xs, desc, sx, wave);
+  __builtin_assume(wave >= 0 && wave < ND * HT);
+  if constexpr (ND == 4) {
+    if (wave >= 3 * HT)
+      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, wave);
+    else if (wave >= 2 * HT)
+      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, wave);
+    else if (wave >= HT)
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, wave);
+    else
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, wave);
+  } else {
+    if (wave >= HT)
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, wave);
+    else
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, wave);
+  }
 }
 
 // Combines the per-split partial states (unnormalised O, running max in log2
@@ -811,10 +851,11 @@ template <int DN, int DR>
 hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
   const int nb = p.n_hg * p.n_splits;
   const int blocks = (p.T >= 8 ? ((p.T + 7) / 8) * 8 : p.T) * nb;
+  constexpr int kNd = Cfg<DN, DR>::NBLK == 4 ? 4 : 2;   // dim parts of the 32-head shape
   if (p.ht == 4)
-    hipLaunchKernelGGL((attn_kernel<DN, DR, 4>), dim3(blocks), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<DN, DR, 4, 2>), dim3(blocks), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_kernel<DN, DR, 2>), dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<DN, DR, 2, kNd>), dim3(blocks), dim3(64 * 2 * kNd), 0, stream, p);
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   static_assert((DN + DR) / 4 <= 128, "one 128-thread team per (query, head)");

@@ -34,7 +34,7 @@ TopkPlan plan_topk(int32_t T, int64_t ld, int32_t k) {
     pl.ok = true;
     return pl;
   }
-  for (int chunk : {4096, 8192, kTopkMaxChunk}) {
+  for (int chunk : {8192, 4096, kTopkMaxChunk}) {
     const int64_t n = ceil_div(ld, chunk);
     if (n * k <= kTopkMaxCand) {
       pl.chunk = chunk;

@@ -8,8 +8,8 @@
 // Design (no locks, no floating-point atomics, deterministic):
 //  * scores become order-preserving uint32 keys; ties are broken by the lower
 //    index, which gives a strict total order (key desc, index asc);
-//  * stage 1: one workgroup (512 threads) per (row, chunk of <= 16384
-//    entries).  Every thread keeps a contiguous segment of SEG keys in
+//  * stage 1: one workgroup (512 threads, or 1024 when rows x chunks are
+//    fewer than the CUs) per (row, chunk of <= 16384 entries).  Every thread keeps a contiguous segment of SEG keys in
 //    registers.  An MSB-first radix select finds the chunk's k-th key: it
 //    starts at the highest bit where the chunk's smallest and largest keys
 //    differ (the bits above are shared by every key, and starting there
@@ -33,21 +33,24 @@ namespace csa {
 
 namespace {
 
-constexpr int kTopkBlock = 512;
-constexpr int kTopkWaves = kTopkBlock / 64;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 
+// BLOCK threads per workgroup (512 or 1024): rows that are few get the
+// larger workgroup, so each thread holds and scans half as many keys.
+template <int BLOCK>
 struct TopkShared {
+  static constexpr int kWaves = BLOCK / 64;
   int hist[kBins];
-  int wsum[kTopkWaves];
+  int wsum[kWaves];
   int sel[4];
-  uint32_t red[2][kTopkWaves];
+  uint32_t red[2][kWaves];
 };
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
 // the sum of all.  Contains barriers: every thread must call it.
-__device__ int block_exclusive_scan(int v, TopkShared& sh, int* total) {
+template <int BLOCK>
+__device__ int block_exclusive_scan(int v, TopkShared<BLOCK>& sh, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int x = v;
@@ -60,7 +63,7 @@ __device__ int block_exclusive_scan(int v, TopkShared& sh, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < TopkShared<BLOCK>::kWaves; ++w) {
     const int s = sh.wsum[w];
     before += (w < wave) ? s : 0;
     tot += s;
@@ -80,8 +83,9 @@ struct Sel {
 
 // K-th largest among the valid keys of the workgroup (1 <= K <= count); bit j
 // of `valid` marks key j of this thread's segment.
-template <int SEG>
-__device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, TopkShared& sh) {
+template <int BLOCK, int SEG>
+__device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, TopkShared<BLOCK>& sh) {
+  constexpr int kBpt = kBins / BLOCK;   // histogram bins per thread in the scan
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // smallest / largest valid key of the workgroup
@@ -106,7 +110,7 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
   kmin = sh.red[0][0];
   kmax = sh.red[1][0];
 #pragma unroll
-  for (int w = 1; w < kTopkWaves; ++w) {
+  for (int w = 1; w < TopkShared<BLOCK>::kWaves; ++w) {
     kmin = min(kmin, sh.red[0][w]);
     kmax = max(kmax, sh.red[1][w]);
   }
@@ -126,19 +130,19 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
     const int nb = top + 1 < kDigitBits ? top + 1 : kDigitBits;
     const int lo = top - nb + 1;
     const uint32_t dmask = (1u << nb) - 1u;
-    for (int i = threadIdx.x; i < kBins; i += kTopkBlock) sh.hist[i] = 0;
+    for (int i = threadIdx.x; i < kBins; i += BLOCK) sh.hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
       if (((valid >> j) & 1u) && (key[j] & s.pmask) == s.prefix) atomicAdd(&sh.hist[(key[j] >> lo) & dmask], 1);
     }
     __syncthreads();
-    // thread t owns bins 2047-4t .. 2044-4t (descending digit order)
-    int c[4];
+    // thread t owns bins 2047 - kBpt t - i, i < kBpt (descending digit order)
+    int c[kBpt];
     int tsum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[i] = sh.hist[kBins - 1 - (4 * threadIdx.x + i)];
+    for (int i = 0; i < kBpt; ++i) {
+      c[i] = sh.hist[kBins - 1 - (kBpt * threadIdx.x + i)];
       tsum += c[i];
     }
     int tot;
@@ -146,9 +150,9 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
     if (before < rem && rem <= before + tsum) {
       int acc = before;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kBpt; ++i) {
         if (acc < rem && rem <= acc + c[i]) {
-          sh.sel[0] = kBins - 1 - (4 * threadIdx.x + i);
+          sh.sel[0] = kBins - 1 - (kBpt * threadIdx.x + i);
           sh.sel[1] = acc;
           sh.sel[2] = c[i];
         }
@@ -172,8 +176,8 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
 
 // Ordered compaction: out_fn(rank, j) for every selected key j of this
 // thread's segment; ranks run 0..K-1 in ascending position.
-template <int SEG, typename OutFn>
-__device__ void emit_selected(const uint32_t (&key)[SEG], uint32_t valid, const Sel& s, TopkShared& sh,
+template <int BLOCK, int SEG, typename OutFn>
+__device__ void emit_selected(const uint32_t (&key)[SEG], uint32_t valid, const Sel& s, TopkShared<BLOCK>& sh,
                               OutFn out_fn) {
   int gt = 0, eq = 0;
 #pragma unroll
@@ -203,9 +207,9 @@ __device__ void emit_selected(const uint32_t (&key)[SEG], uint32_t valid, const 
   }
 }
 
-template <int SEG>
-__global__ __launch_bounds__(kTopkBlock) void topk_chunk_kernel(TopkParams p) {
-  __shared__ TopkShared sh;
+template <int BLOCK, int SEG>
+__global__ __launch_bounds__(BLOCK) void topk_chunk_kernel(TopkParams p) {
+  __shared__ TopkShared<BLOCK> sh;
   const int t = blockIdx.x / p.n_chunks;
   const int ch = blockIdx.x - t * p.n_chunks;
   const int nv = (int)max<int64_t>(0, min<int64_t>(p.n_visible[t], p.ld));
@@ -232,26 +236,26 @@ __global__ __launch_bounds__(kTopkBlock) void topk_chunk_kernel(TopkParams p) {
   if (p.n_chunks == 1) {
     int32_t* o = p.out + (size_t)t * p.k;
     if (K > 0) {
-      const Sel s = radix_select<SEG>(key, valid, K, sh);
-      emit_selected<SEG>(key, valid, s, sh, [&](int rank, int j) {
+      const Sel s = radix_select<BLOCK, SEG>(key, valid, K, sh);
+      emit_selected<BLOCK, SEG>(key, valid, s, sh, [&](int rank, int j) {
         if (rank < K) o[rank] = c0 + i0 + j;
       });
     }
-    for (int i = K + threadIdx.x; i < p.k; i += kTopkBlock) o[i] = -1;
+    for (int i = K + threadIdx.x; i < p.k; i += BLOCK) o[i] = -1;
   } else {
     const size_t base = ((size_t)t * p.n_chunks + ch) * p.k;
     uint32_t* ck = p.cand_key + base;
     int32_t* ci = p.cand_idx + base;
     if (K > 0) {
-      const Sel s = radix_select<SEG>(key, valid, K, sh);
-      emit_selected<SEG>(key, valid, s, sh, [&](int rank, int j) {
+      const Sel s = radix_select<BLOCK, SEG>(key, valid, K, sh);
+      emit_selected<BLOCK, SEG>(key, valid, s, sh, [&](int rank, int j) {
         if (rank < K) {
           ck[rank] = key[j];
           ci[rank] = c0 + i0 + j;
         }
       });
     }
-    for (int i = K + threadIdx.x; i < p.k; i += kTopkBlock) {
+    for (int i = K + threadIdx.x; i < p.k; i += BLOCK) {
       ck[i] = 0u;
       ci[i] = -1;
     }
@@ -260,9 +264,9 @@ __global__ __launch_bounds__(kTopkBlock) void topk_chunk_kernel(TopkParams p) {
 
 // Candidates of a row arrive in chunk order and ascending index within each
 // chunk, so position order is index order; empty slots (index -1) are masked.
-template <int SEG>
-__global__ __launch_bounds__(kTopkBlock) void topk_merge_kernel(TopkParams p) {
-  __shared__ TopkShared sh;
+template <int BLOCK, int SEG>
+__global__ __launch_bounds__(BLOCK) void topk_merge_kernel(TopkParams p) {
+  __shared__ TopkShared<BLOCK> sh;
   const int t = blockIdx.x;
   const int ncand = p.n_chunks * p.k;
   const int i0 = threadIdx.x * SEG;
@@ -302,47 +306,59 @@ __global__ __launch_bounds__(kTopkBlock) void topk_merge_kernel(TopkParams p) {
   const int K = min(p.k, total);
   int32_t* o = p.out + (size_t)t * p.k;
   if (K > 0) {
-    const Sel s = radix_select<SEG>(key, valid, K, sh);
-    emit_selected<SEG>(key, valid, s, sh, [&](int rank, int j) {
+    const Sel s = radix_select<BLOCK, SEG>(key, valid, K, sh);
+    emit_selected<BLOCK, SEG>(key, valid, s, sh, [&](int rank, int j) {
       if (rank < K) o[rank] = idx[j];
     });
   }
-  for (int i = K + threadIdx.x; i < p.k; i += kTopkBlock) o[i] = -1;
+  for (int i = K + threadIdx.x; i < p.k; i += BLOCK) o[i] = -1;
 }
 
-template <int SEG>
+template <int BLOCK, int SEG>
 hipError_t launch_chunk(const TopkParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_chunk_kernel<SEG>, dim3(p.T * p.n_chunks), dim3(kTopkBlock), 0, stream, p);
+  hipLaunchKernelGGL((topk_chunk_kernel<BLOCK, SEG>), dim3(p.T * p.n_chunks), dim3(BLOCK), 0, stream, p);
   return hipPeekAtLastError();
 }
-template <int SEG>
+template <int BLOCK, int SEG>
 hipError_t launch_merge(const TopkParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_merge_kernel<SEG>, dim3(p.T), dim3(kTopkBlock), 0, stream, p);
+  hipLaunchKernelGGL((topk_merge_kernel<BLOCK, SEG>), dim3(p.T), dim3(BLOCK), 0, stream, p);
   return hipPeekAtLastError();
 }
 
-int seg_for(int n) {
-  const int per = (n + kTopkBlock - 1) / kTopkBlock;
+// keys per thread for n keys over a workgroup of `block` threads
+int seg_for(int n, int block) {
+  const int per = (n + block - 1) / block;
   return per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : 32;
+}
+
+template <int BLOCK>
+hipError_t launch_chunk_b(const TopkParams& p, hipStream_t stream) {
+  switch (seg_for(p.chunk, BLOCK)) {
+    case 4: return launch_chunk<BLOCK, 4>(p, stream);
+    case 8: return launch_chunk<BLOCK, 8>(p, stream);
+    case 16: return launch_chunk<BLOCK, 16>(p, stream);
+    default: return launch_chunk<BLOCK, 32>(p, stream);
+  }
+}
+template <int BLOCK>
+hipError_t launch_merge_b(const TopkParams& p, hipStream_t stream) {
+  switch (seg_for(p.n_chunks * p.k, BLOCK)) {
+    case 4: return launch_merge<BLOCK, 4>(p, stream);
+    case 8: return launch_merge<BLOCK, 8>(p, stream);
+    case 16: return launch_merge<BLOCK, 16>(p, stream);
+    default: return launch_merge<BLOCK, 32>(p, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
-  hipError_t e;
-  switch (seg_for(p.chunk)) {
-    case 4: e = launch_chunk<4>(p, stream); break;
-    case 8: e = launch_chunk<8>(p, stream); break;
-    case 16: e = launch_chunk<16>(p, stream); break;
-    default: e = launch_chunk<32>(p, stream); break;
-  }
+  // fewer workgroups than CUs, and more than four keys per thread at 512
+  // threads: 1024 threads each
+  const bool wide = (int64_t)p.T * p.n_chunks < 256 && p.chunk > 4 * 512;
+  const hipError_t e = wide ? launch_chunk_b<1024>(p, stream) : launch_chunk_b<512>(p, stream);
   if (e != hipSuccess || p.n_chunks == 1) return e;
-  switch (seg_for(p.n_chunks * p.k)) {
-    case 4: return launch_merge<4>(p, stream);
-    case 8: return launch_merge<8>(p, stream);
-    case 16: return launch_merge<16>(p, stream);
-    default: return launch_merge<32>(p, stream);
-  }
+  return p.T < 256 ? launch_merge_b<1024>(p, stream) : launch_merge_b<512>(p, stream);
 }
 
 }  // namespace csa

@@ -54,8 +54,10 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     # rows that fit one chunk need no top-k workspace
     assert csa.csa_topk_workspace_size(64, 8192, 512) == 0
-    # 131072-entry rows: 32 chunks of 4096, 512 candidates each
-    assert csa.csa_topk_workspace_size(4, 131072, 512) == 4 * 32 * 512 * 8
+    # 131072-entry rows: 16 chunks of 8192, 512 candidates each
+    assert csa.csa_topk_workspace_size(4, 131072, 512) == 4 * 16 * 512 * 8
+    # 32 candidates per chunk: up to 512 chunks of 8192 fit the merge
+    assert csa.csa_topk_workspace_size(2, 512 * 8192, 32) == 2 * 512 * 32 * 8
     # rows too long for two levels of 16384 candidates
     assert csa.csa_topk_workspace_size(1, 1 << 22, 2048) == 0
     # many queries: one workgroup per (query, 32 heads), no split
