@@ -13,18 +13,19 @@
 //    cache (no Python loop, no BF16 materialisation); E4: (o, lse); E5: batch
 //    in the grid.
 //
-// Mapping on gfx950 (256 threads = 4 waves per workgroup):
-//  * a workgroup owns one query, 32 heads and a range of key slots (the range
-//    is split over workgroups only when there are few queries);
-//  * wave (ht, dh): heads [16 ht, 16 ht + 16) of the group and one half of
-//    the latent dims (dh = 0: the first nope blocks; dh = 1: the remaining
-//    nope dims and the rope dims).  Every 64-key tile is handled whole by
-//    both waves of a head tile: each computes the scores over its own dims,
-//    the two partial score tiles are added through LDS, both run the same
-//    online softmax (bit-identical state), and each accumulates O for its
-//    own dims only.  O and q of a wave are half of a head tile's, which
-//    keeps a wave's registers small, and no merge of softmax states is
-//    needed at the end;
+// Mapping on gfx950 (eight waves per workgroup, two per SIMD):
+//  * a workgroup owns one query, HT x 16 heads and a range of key slots (the
+//    range is split over workgroups only when there are few queries);
+//  * wave (ht, dp): heads [16 ht, 16 ht + 16) of the group and dim part dp of
+//    ND parts of the latent.  Few queries: HT = 2, ND = 4 (part dp < 3 owns
+//    nope block dp, part 3 the last 64 nope dims and the rope dims).  Many
+//    queries: HT = 4, ND = 2 (dim halves).  Every 64-key tile is handled
+//    whole by all parts of a head tile: each computes the scores over its own
+//    dims, the partial score tiles are added through LDS in one fixed order,
+//    all parts run the same online softmax (bit-identical state), and each
+//    accumulates O for its own dims only.  O and q of a wave are a part of a
+//    head tile's, which keeps a wave's registers small enough for two waves
+//    per SIMD, and no merge of softmax states is needed at the end;
 //  * gather: key descriptors (top-k index -> page table -> row, or window slot
 //    -> row) are resolved once into LDS; each 64-key tile is copied from HBM
 //    straight into LDS with global_load_lds_dwordx4 (no register staging),
@@ -34,10 +35,10 @@
 //    bytes of their rows), so it touches 16 cache lines instead of 64, and
 //    every lane keeps one key for all of its DMAs.  Inside a block the key
 //    rows are XOR-ed with 8 on alternate blocks, which keeps the QK reads and
-//    both transpose reads free of LDS bank conflicts.  Rows of masked keys
-//    (padding, invalid entries, the ragged tail)
-//    are cleared in LDS once their DMA has landed, so no operand needs a
-//    per-key mask.  The cache's FP8/BF16 bytes go to the MFMA unchanged;
+//    both transpose reads free of LDS bank conflicts.  Masked keys (padding,
+//    invalid entries, the ragged tail) copy a static row of zeros, so no
+//    operand needs a per-key mask.  The cache's FP8/BF16 bytes go to the MFMA
+//    unchanged;
 //  * QK: S^T (keys x heads) = X . Q^T on v_mfma 16x16x128 FP8, with q split
 //    into two E4M3 terms hi + lo sharing a power-of-two per-head scale (the K
 //    dimension is [hi | lo], X read once and used for both), plus the rope
@@ -67,8 +68,7 @@ struct Cfg {
   static constexpr int NFB = DN / 128;                       // full 128-dim nope blocks
   static constexpr int REM = DN % 128;                       // combined hi|lo block (<= 64 dims)
   static constexpr int NBLK = NFB + (REM > 0 ? 1 : 0);
-  static constexpr int B0 = (NBLK + 1) / 2;                  // nope blocks of dim half 0
-  static constexpr int N0 = DN < 128 * B0 ? DN : 128 * B0;   // nope dims of dim half 0
+  static constexpr int B0 = (NBLK + 1) / 2;                  // nope blocks of dim half 0 (ND = 2)
   static constexpr int CHN = DN / 16;                        // 16-byte nope chunks of a row
   static constexpr int CHR = DR / 8;                         // 16-byte rope chunks of a row
   static constexpr int CHNP = (CHN + 3) & ~3;                // padded to whole quads
@@ -177,7 +177,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   const bool prefill = p.prefill_seq >= 0;
   const int t = bk.t, seq = bk.seq, kv0 = bk.kv0, nkeys = bk.nkeys, n_sel = bk.n_sel, sel_end = bk.sel_end;
 
-  // ---- query rows of this dim half (packed BF16), issued first so that
+  // ---- query rows of this dim part (packed BF16), issued first so that
   // their latency overlaps the descriptor round trips
   v4i qraw[HF::NQB > 0 ? HF::NQB : 1][4];
   v4i qrope[HF::NR > 0 ? HF::NR : 1];
@@ -327,7 +327,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   }
 
   // ---- query operands: q split into two E4M3 terms hi + lo with a shared
-  // power-of-two per-head scale over this half's nope dims
+  // power-of-two per-head scale over this part's nope dims
   v8i qhi[HF::FB > 0 ? HF::FB : 1], qlo[HF::FB > 0 ? HF::FB : 1], qcomb;
   v8bf qr[HF::NR > 0 ? HF::NR : 1];
   float cq = 0.0f;
@@ -409,74 +409,74 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 
   // ---- one tile's steps
   v4f acc[4], racc[4];
-  // QK: partial scores over this half's dims of the tile in buffer xq
+  // QK: partial scores over this part's dims of the tile in buffer xq
   auto qk = [&](const uint8_t* xq) {
-      // -- partial scores over this half's dims: four 16-key subtiles; the
-      //    operands of the next step are read before the MFMAs of this one
-  #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        acc[st] = (v4f){0.f, 0.f, 0.f, 0.f};
-        racc[st] = acc[st];
-      }
-      if (tile_ok) {
-        constexpr int NSTEP = HF::FB + (HF::COMB ? 1 : 0);
-        auto read_step = [&](int step, v8i (&x)[4]) {
-  #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            if (step < HF::FB) {
-              // chunks 8 (FB0 + step) + 2 g and + 1 (even, odd)
-              const uint8_t* base = xq + (HF::FB0 + step) * 8192 + qk_g;
-              const v4i lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
-              const v4i hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
-              x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-              // chunks 8 NFB + 2 (g & 1) and + 1
-              const uint8_t* base = xq + C::NFB * 8192 + 512 * (g & 1);
-              v4i lo = (v4i){0, 0, 0, 0}, hi = lo;
-              if (32 * (g & 1) < C::REM) lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
-              if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
-              x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-          }
-        };
-        v8i x[2][4];
-        v4i y[HF::NR > 0 ? HF::NR : 1][4];
-        if (NSTEP > 0) read_step(0, x[0]);
-  #pragma unroll
-        for (int rr = 0; rr < HF::NR; ++rr) {
-          // rope chunk CHNP + 4 rr + g (parity g & 1)
-          const uint8_t* base = xq + ((C::CHNP / 4 + rr) * 16 + g) * 256;
-  #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            y[rr][st] = (v4i){0, 0, 0, 0};
-            if (32 * rr + 8 * g < DR) y[rr][st] = *reinterpret_cast<const v4i*>(base + qk_off[st][g & 1]);
-          }
-        }
-  #pragma unroll
-        for (int step = 0; step < NSTEP; ++step) {
-          if (step + 1 < NSTEP) read_step(step + 1, x[(step + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
+    // -- partial scores over this part's dims: four 16-key subtiles; the
+    //    operands of the next step are read before the MFMAs of this one
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      acc[st] = (v4f){0.f, 0.f, 0.f, 0.f};
+      racc[st] = acc[st];
+    }
+    if (tile_ok) {
+      constexpr int NSTEP = HF::FB + (HF::COMB ? 1 : 0);
+      auto read_step = [&](int step, v8i (&x)[4]) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
           if (step < HF::FB) {
-  #pragma unroll
-            for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qhi[step], acc[st]);
-  #pragma unroll
-            for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qlo[step], acc[st]);
+            // chunks 8 (FB0 + step) + 2 g and + 1 (even, odd)
+            const uint8_t* base = xq + (HF::FB0 + step) * 8192 + qk_g;
+            const v4i lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
+            const v4i hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
+            x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           } else {
-  #pragma unroll
-            for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qcomb, acc[st]);
+            // chunks 8 NFB + 2 (g & 1) and + 1
+            const uint8_t* base = xq + C::NFB * 8192 + 512 * (g & 1);
+            v4i lo = (v4i){0, 0, 0, 0}, hi = lo;
+            if (32 * (g & 1) < C::REM) lo = *reinterpret_cast<const v4i*>(base + qk_off[st][0]);
+            if (32 * (g & 1) + 16 < C::REM) hi = *reinterpret_cast<const v4i*>(base + 256 + qk_off[st][1]);
+            x[st] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
-  #pragma unroll
-        for (int rr = 0; rr < HF::NR; ++rr)
-  #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            racc[st] = mfma_bf16_32(__builtin_bit_cast(v8bf, y[rr][st]), qr[rr], racc[st]);
+      };
+      v8i x[2][4];
+      v4i y[HF::NR > 0 ? HF::NR : 1][4];
+      if (NSTEP > 0) read_step(0, x[0]);
+#pragma unroll
+      for (int rr = 0; rr < HF::NR; ++rr) {
+        // rope chunk CHNP + 4 rr + g (parity g & 1)
+        const uint8_t* base = xq + ((C::CHNP / 4 + rr) * 16 + g) * 256;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          y[rr][st] = (v4i){0, 0, 0, 0};
+          if (32 * rr + 8 * g < DR) y[rr][st] = *reinterpret_cast<const v4i*>(base + qk_off[st][g & 1]);
+        }
       }
+#pragma unroll
+      for (int step = 0; step < NSTEP; ++step) {
+        if (step + 1 < NSTEP) read_step(step + 1, x[(step + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (step < HF::FB) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qhi[step], acc[st]);
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qlo[step], acc[st]);
+        } else {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[st] = mfma_f8_128(x[step & 1][st], qcomb, acc[st]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int rr = 0; rr < HF::NR; ++rr)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          racc[st] = mfma_bf16_32(__builtin_bit_cast(v8bf, y[rr][st]), qr[rr], racc[st]);
+    }
   };
   // valid keys of tile `it` (the same in every wave): bit k = key k.  Masked
   // keys were copied from a zero row, so they add nothing to S or O; dim
-  // half 0 gives them -inf in the exchanged score.
+  // part 0 gives them -inf in the exchanged score.
   auto tile_mask = [&](int it) -> uint64_t {
     const int sk = it * kAttnTile + lane;
     const int dk = sk < nkeys ? desc[sk] : -1;
@@ -485,156 +485,156 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   // own partial (scaled) of the exchanged score
   auto own_part = [&](uint64_t vmask, bool tile_swa, v4f (&part)[4]) {
     const bool full = vmask == ~0ull;
-      // -- own partial (scaled), exchanged with the other dim half of the head
-      //    tile.  Half 0 also subtracts the running max (so the sum S' is the
-      //    exp2 argument) and carries -inf for masked keys (lane keys
-      //    16 st + 4 g + i).
-      const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
-      const float ks = tile_swa ? cqs : cql;
-  #pragma unroll
+    // -- own partial (scaled), exchanged with the other dim parts of the
+    //    head tile.  Part 0 also subtracts the running max (so the sum S' is
+    //    the exp2 argument) and carries -inf for masked keys (lane keys
+    //    16 st + 4 g + i).
+    const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+    const float ks = tile_swa ? cqs : cql;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (DP == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[st][i] = __builtin_fmaf(acc[st][i], ks, -msub);
+      } else {
+        part[st] = acc[st] * ks + racc[st] * cr;
+      }
+    }
+    if (DP == 0 && !full) {
+#pragma unroll
       for (int st = 0; st < 4; ++st) {
-        if (DP == 0) {
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) part[st][i] = __builtin_fmaf(acc[st][i], ks, -msub);
-        } else {
-          part[st] = acc[st] * ks + racc[st] * cr;
-        }
+        const uint32_t vw = st < 2 ? (uint32_t)vmask : (uint32_t)(vmask >> 32);
+        const uint32_t bits = vw >> (16 * (st & 1) + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((bits >> i) & 1u)) part[st][i] = -__builtin_inff();
       }
-      if (DP == 0 && !full) {
-  #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const uint32_t vw = st < 2 ? (uint32_t)vmask : (uint32_t)(vmask >> 32);
-          const uint32_t bits = vw >> (16 * (st & 1) + 4 * g);
-  #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!((bits >> i) & 1u)) part[st][i] = -__builtin_inff();
-        }
-      }
+    }
   };
   // online softmax and PV of tile `it` (tot: the exchanged score, summed over
   // the dim parts in the same order in every part)
   auto soft_pv = [&](int it, const v4f (&tot)[4], const uint8_t* xb, bool tile_swa) {
     const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // as subtracted in own_part
-      if (tile_ok) {
-        // -- online softmax (lane: head h, keys 16 st + 4 g + i); sv = S - msub
-        float sv[16];
-        float tmax = -__builtin_inff();
-  #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sv[4 * st + i] = tot[st][i];
-            tmax = fmaxf(tmax, tot[st][i]);
-          }
+    if (tile_ok) {
+      // -- online softmax (lane: head h, keys 16 st + 4 g + i); sv = S - msub
+      float sv[16];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[4 * st + i] = tot[st][i];
+          tmax = fmaxf(tmax, tot[st][i]);
         }
-        tmax = max_over_groups(tmax);
-        const bool m_inf = m_run == -__builtin_inff();
-        const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
-        float pr[16];
-        float psum = 0.0f;
-        if (__ballot(grow)) {
-          // raise the running max to the tile max on the lanes that grew
-          const float delta = grow ? tmax : 0.0f;
-          const float alpha = grow ? (m_inf ? 0.0f : __builtin_amdgcn_exp2f(-tmax)) : 1.0f;
-          if (grow) m_run = msub + tmax;
-          l_run *= alpha;
-          if (it > 0) {
-  #pragma unroll
-            for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
-          }
-  #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            pr[e] = __builtin_amdgcn_exp2f(sv[e] - delta);
-            psum += pr[e];
-          }
-        } else {
-  #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            pr[e] = __builtin_amdgcn_exp2f(sv[e]);   // exp2(-inf) = 0 for masked keys
-            psum += pr[e];
-          }
+      }
+      tmax = max_over_groups(tmax);
+      const bool m_inf = m_run == -__builtin_inff();
+      const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
+      float pr[16];
+      float psum = 0.0f;
+      if (__ballot(grow)) {
+        // raise the running max to the tile max on the lanes that grew
+        const float delta = grow ? tmax : 0.0f;
+        const float alpha = grow ? (m_inf ? 0.0f : __builtin_amdgcn_exp2f(-tmax)) : 1.0f;
+        if (grow) m_run = msub + tmax;
+        l_run *= alpha;
+        if (it > 0) {
+#pragma unroll
+          for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
         }
-        l_run += psum;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          pr[e] = __builtin_amdgcn_exp2f(sv[e] - delta);
+          psum += pr[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          pr[e] = __builtin_amdgcn_exp2f(sv[e]);   // exp2(-inf) = 0 for masked keys
+          psum += pr[e];
+        }
+      }
+      l_run += psum;
 
-        // -- P operand for nope: bytes [hi of the lane's 16 keys | lo of them]
-        //    of p x key-scale ratio x 2^(8 - tau); lo = the rounding residual
-        const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
-        v8i pb;
-  #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const float x0 = pr[4 * st] * kq, x1 = pr[4 * st + 1] * kq;
-          const float x2 = pr[4 * st + 2] * kq, x3 = pr[4 * st + 3] * kq;
-          const int w = pack4_fp8(x0, x1, x2, x3);
-          const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-          const v2f b23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-          pb[st] = w;
-          pb[4 + st] = pack4_fp8(x0 - b01[0], x1 - b01[1], x2 - b23[0], x3 - b23[1]);
-        }
+      // -- P operand for nope: bytes [hi of the lane's 16 keys | lo of them]
+      //    of p x key-scale ratio x 2^(8 - tau); lo = the rounding residual
+      const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
+      v8i pb;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float x0 = pr[4 * st] * kq, x1 = pr[4 * st + 1] * kq;
+        const float x2 = pr[4 * st + 2] * kq, x3 = pr[4 * st + 3] * kq;
+        const int w = pack4_fp8(x0, x1, x2, x3);
+        const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const v2f b23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        pb[st] = w;
+        pb[4 + st] = pack4_fp8(x0 - b01[0], x1 - b01[1], x2 - b23[0], x3 - b23[1]);
+      }
 
-        // -- PV: O^T[dims x heads] += X^T[dims x K] P^T[K x heads]; A = the
-        //    two 8-key transpose reads, used for the hi and the lo half of K.
-        //    Reads of the next batch go out before the MFMAs of this one.
-        {
-          constexpr int PB = 4;   // dim tiles per batch
-          constexpr int NB = (HF::NPT + PB - 1) / PB;
-          v2i ra[2][PB], rb[2][PB];
-          auto read_batch = [&](int bt, v2i (&a)[PB], v2i (&b)[PB]) {
-  #pragma unroll
-            for (int j = 0; j < PB; ++j) {
-              const int dt = bt * PB + j;
-              if (dt < HF::NPT) {
-                const int c = HF::PT0 + dt;
-                const uint8_t* cb = xb + chunk_base(c);
-                a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[0][c & 1]));
-                b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[1][c & 1]));
-              }
+      // -- PV: O^T[dims x heads] += X^T[dims x K] P^T[K x heads]; A = the
+      //    two 8-key transpose reads, used for the hi and the lo half of K.
+      //    Reads of the next batch go out before the MFMAs of this one.
+      {
+        constexpr int PB = 4;   // dim tiles per batch
+        constexpr int NB = (HF::NPT + PB - 1) / PB;
+        v2i ra[2][PB], rb[2][PB];
+        auto read_batch = [&](int bt, v2i (&a)[PB], v2i (&b)[PB]) {
+#pragma unroll
+          for (int j = 0; j < PB; ++j) {
+            const int dt = bt * PB + j;
+            if (dt < HF::NPT) {
+              const int c = HF::PT0 + dt;
+              const uint8_t* cb = xb + chunk_base(c);
+              a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[0][c & 1]));
+              b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[1][c & 1]));
             }
-          };
-          if (NB > 0) read_batch(0, ra[0], rb[0]);
-  #pragma unroll
-          for (int bt = 0; bt < NB; ++bt) {
-            if (bt + 1 < NB) read_batch(bt + 1, ra[(bt + 1) & 1], rb[(bt + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-            for (int j = 0; j < PB; ++j) {
-              const int dt = bt * PB + j;
-              if (dt < HF::NPT) {
-                const v2i a0 = ra[bt & 1][j], a1 = rb[bt & 1][j];
-                const v8i a = (v8i){a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};
-                O[dt] = mfma_f8_128(a, pb, O[dt]);
-              }
-            }
-            __builtin_amdgcn_sched_barrier(0);
           }
-        }
-        if (HF::NRT > 0) {
-          // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7); rope dim tile
-          // j = chunks CHNP + 2 j (+1)
-          v4i pbf[2];
-  #pragma unroll
-          for (int u = 0; u < 2; ++u)
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) pbf[u][e] = (int)pack2_bf16(pr[8 * u + 2 * e], pr[8 * u + 2 * e + 1]);
-          v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
-  #pragma unroll
-          for (int j = 0; j < HF::NRT; ++j) {
-            const uint8_t* cb = xb + ((C::CHNP / 4 + (j >> 1)) * 16 + 2 * (j & 1)) * 256;
-  #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const v2i lo = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][0])));
-              const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][1])));
-              ya[j][u] = (v4i){lo[0], lo[1], hi[0], hi[1]};
+        };
+        if (NB > 0) read_batch(0, ra[0], rb[0]);
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt) {
+          if (bt + 1 < NB) read_batch(bt + 1, ra[(bt + 1) & 1], rb[(bt + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < PB; ++j) {
+            const int dt = bt * PB + j;
+            if (dt < HF::NPT) {
+              const v2i a0 = ra[bt & 1][j], a1 = rb[bt & 1][j];
+              const v8i a = (v8i){a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};
+              O[dt] = mfma_f8_128(a, pb, O[dt]);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-          for (int u = 0; u < 2; ++u)
-  #pragma unroll
-            for (int j = 0; j < HF::NRT; ++j)
-              O[HF::NPT + j] = mfma_bf16_32(__builtin_bit_cast(v8bf, ya[j][u]), __builtin_bit_cast(v8bf, pbf[u]),
-                                            O[HF::NPT + j]);
         }
       }
+      if (HF::NRT > 0) {
+        // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7); rope dim tile
+        // j = chunks CHNP + 2 j (+1)
+        v4i pbf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pbf[u][e] = (int)pack2_bf16(pr[8 * u + 2 * e], pr[8 * u + 2 * e + 1]);
+        v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
+#pragma unroll
+        for (int j = 0; j < HF::NRT; ++j) {
+          const uint8_t* cb = xb + ((C::CHNP / 4 + (j >> 1)) * 16 + 2 * (j & 1)) * 256;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const v2i lo = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][0])));
+            const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][1])));
+            ya[j][u] = (v4i){lo[0], lo[1], hi[0], hi[1]};
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < HF::NRT; ++j)
+            O[HF::NPT + j] = mfma_bf16_32(__builtin_bit_cast(v8bf, ya[j][u]), __builtin_bit_cast(v8bf, pbf[u]),
+                                          O[HF::NPT + j]);
+      }
+    }
   };
 
   // ---- the tiles: a barrier for each tile's arrival and one for the score
@@ -678,7 +678,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   }
   if (!tile_ok) return;
 
-  // ---- output of this half's dims (the softmax state is the same in both halves)
+  // ---- output of this part's dims (the softmax state is the same in every part)
   const float L = sum_over_groups(l_run);
   const float M = m_run;
   const bool final_out = p.n_splits == 1;

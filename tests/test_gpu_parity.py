@@ -141,6 +141,22 @@ def test_decode_fewer_stored_entries_than_position_allows():
     check_full(dataclasses.replace(wl, n_comp=n_comp))
 
 
+def test_partial_head_tiles_production_dims():
+    # 40 heads at the production latent: the second 32-head workgroup has one
+    # head tile with 8 valid heads and one with none, and every tile runs on
+    # four dim-part waves
+    say("case decode 40 heads (partial head tiles)")
+    spec = ci.small_spec(name="small_h40", ctx_lens=[3000, 1212, 2400], H=40, shuffle_pages=True)
+    check_full(ci.generate(spec, seed=115))
+
+
+def test_single_tile_key_range():
+    # top-k 16 and a 32-token window: 64 key slots, one tile per workgroup
+    say("case decode single tile (k 16, window 32)")
+    spec = ci.small_spec(name="small_one_tile", ctx_lens=[2000, 640], k=16, W=32)
+    check_full(ci.generate(spec, seed=116))
+
+
 def test_ring_permutation_invariance_gpu():
     say("case ring permutation")
     wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1800]), seed=105)
