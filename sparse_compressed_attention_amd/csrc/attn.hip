@@ -161,7 +161,7 @@ struct Block {
 
 template <int DN, int DR, int DP, int HT, int ND>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, uint8_t* xs0, int32_t* desc,
-                                          v4f* sx, int wave) {
+                                          v4f* sx, v4i* px, int wave) {
   using C = Cfg<DN, DR>;
   using HF = Part<DN, DR, ND, DP>;
   constexpr int D = DN + DR;
@@ -378,7 +378,8 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   const bool sink_here = bk.split == 0 && head_ok;
   const float sink2 = head_ok ? sink_raw * kLog2e : -__builtin_inff();
   float m_run = sink_here ? sink2 : -__builtin_inff();
-  float l_run = (sink_here && g == 0 && sink2 > -__builtin_inff()) ? 1.0f : 0.0f;
+  // (with split P the sink's share of the denominator is counted by part 0)
+  float l_run = (sink_here && g == 0 && sink2 > -__builtin_inff() && (ND != 4 || DP == 0)) ? 1.0f : 0.0f;
   v4f O[HF::NO];
 #pragma unroll
   for (int i = 0; i < HF::NO; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -513,127 +514,134 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   };
   // online softmax and PV of tile `it` (tot: the exchanged score, summed over
   // the dim parts in the same order in every part)
-  auto soft_pv = [&](int it, const v4f (&tot)[4], const uint8_t* xb, bool tile_swa) {
+  // With four dim parts, each part exponentiates and packs the
+  // probabilities of one 16-key subtile only (the max still comes from the
+  // whole tile, so every part takes the same rescale decisions), and the
+  // parts swap their P through LDS; the denominator is kept per part and
+  // summed at the end.
+  constexpr bool kSplitP = ND == 4;
+  // online softmax of tile `it` (tot: the exchanged score, summed over the
+  // dim parts in the same order in every part); P of subtile st, when this
+  // part computes it, is pq[st] = (hi, lo E4M3 of p x kq; p as two BF16 pairs)
+  auto soft = [&](int it, const v4f (&tot)[4], bool tile_swa, v4i (&pq)[4]) {
     const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // as subtracted in own_part
-    if (tile_ok) {
-      // -- online softmax (lane: head h, keys 16 st + 4 g + i); sv = S - msub
-      float sv[16];
-      float tmax = -__builtin_inff();
+    // -- lane: head h, keys 16 st + 4 g + i; sv = S - msub
+    float sv[16];
+    float tmax = -__builtin_inff();
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[4 * st + i] = tot[st][i];
-          tmax = fmaxf(tmax, tot[st][i]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        sv[4 * st + i] = tot[st][i];
+        tmax = fmaxf(tmax, tot[st][i]);
       }
-      tmax = max_over_groups(tmax);
-      const bool m_inf = m_run == -__builtin_inff();
-      const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
-      float pr[16];
-      float psum = 0.0f;
-      if (__ballot(grow)) {
-        // raise the running max to the tile max on the lanes that grew
-        const float delta = grow ? tmax : 0.0f;
-        const float alpha = grow ? (m_inf ? 0.0f : __builtin_amdgcn_exp2f(-tmax)) : 1.0f;
-        if (grow) m_run = msub + tmax;
-        l_run *= alpha;
-        if (it > 0) {
+    }
+    tmax = max_over_groups(tmax);
+    const bool m_inf = m_run == -__builtin_inff();
+    const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
+    float delta = 0.0f;
+    if (__ballot(grow)) {
+      // raise the running max to the tile max on the lanes that grew
+      delta = grow ? tmax : 0.0f;
+      const float alpha = grow ? (m_inf ? 0.0f : __builtin_amdgcn_exp2f(-tmax)) : 1.0f;
+      if (grow) m_run = msub + tmax;
+      l_run *= alpha;
+      if (it > 0) {
 #pragma unroll
-          for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          pr[e] = __builtin_amdgcn_exp2f(sv[e] - delta);
-          psum += pr[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          pr[e] = __builtin_amdgcn_exp2f(sv[e]);   // exp2(-inf) = 0 for masked keys
-          psum += pr[e];
-        }
+        for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
       }
-      l_run += psum;
-
-      // -- P operand for nope: bytes [hi of the lane's 16 keys | lo of them]
-      //    of p x key-scale ratio x 2^(8 - tau); lo = the rounding residual
-      const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
-      v8i pb;
+    }
+    const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
+    float psum = 0.0f;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float x0 = pr[4 * st] * kq, x1 = pr[4 * st + 1] * kq;
-        const float x2 = pr[4 * st + 2] * kq, x3 = pr[4 * st + 3] * kq;
-        const int w = pack4_fp8(x0, x1, x2, x3);
-        const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-        const v2f b23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-        pb[st] = w;
-        pb[4 + st] = pack4_fp8(x0 - b01[0], x1 - b01[1], x2 - b23[0], x3 - b23[1]);
+    for (int st = 0; st < 4; ++st) {
+      if (kSplitP && st != DP) continue;
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(sv[4 * st + i] - delta);   // exp2(-inf) = 0 for masked keys
+        psum += pr[i];
       }
-
-      // -- PV: O^T[dims x heads] += X^T[dims x K] P^T[K x heads]; A = the
-      //    two 8-key transpose reads, used for the hi and the lo half of K.
-      //    Reads of the next batch go out before the MFMAs of this one.
-      {
-        constexpr int PB = 4;   // dim tiles per batch
-        constexpr int NB = (HF::NPT + PB - 1) / PB;
-        v2i ra[2][PB], rb[2][PB];
-        auto read_batch = [&](int bt, v2i (&a)[PB], v2i (&b)[PB]) {
+      // nope operand bytes: hi of p x key-scale ratio x 2^(8 - tau), lo = the
+      // rounding residual; rope operand: p in BF16
+      const float x0 = pr[0] * kq, x1 = pr[1] * kq, x2 = pr[2] * kq, x3 = pr[3] * kq;
+      const int w = pack4_fp8(x0, x1, x2, x3);
+      const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+      const v2f b23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+      pq[st] = (v4i){w, pack4_fp8(x0 - b01[0], x1 - b01[1], x2 - b23[0], x3 - b23[1]),
+                     (int)pack2_bf16(pr[0], pr[1]), (int)pack2_bf16(pr[2], pr[3])};
+    }
+    l_run += psum;
+  };
+  // PV of the tile in buffer xb with the probabilities pq of all 16-key subtiles
+  auto pv = [&](const uint8_t* xb, const v4i (&pq)[4]) {
+    // -- B operand for nope: bytes [hi of the lane's 16 keys | lo of them]
+    v8i pb;
 #pragma unroll
-          for (int j = 0; j < PB; ++j) {
-            const int dt = bt * PB + j;
-            if (dt < HF::NPT) {
-              const int c = HF::PT0 + dt;
-              const uint8_t* cb = xb + chunk_base(c);
-              a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[0][c & 1]));
-              b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[1][c & 1]));
-            }
+    for (int st = 0; st < 4; ++st) {
+      pb[st] = pq[st][0];
+      pb[4 + st] = pq[st][1];
+    }
+    // -- PV: O^T[dims x heads] += X^T[dims x K] P^T[K x heads]; A = the
+    //    two 8-key transpose reads, used for the hi and the lo half of K.
+    //    Reads of the next batch go out before the MFMAs of this one.
+    {
+      constexpr int PB = 4;   // dim tiles per batch
+      constexpr int NB = (HF::NPT + PB - 1) / PB;
+      v2i ra[2][PB], rb[2][PB];
+      auto read_batch = [&](int bt, v2i (&a)[PB], v2i (&b)[PB]) {
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const int dt = bt * PB + j;
+          if (dt < HF::NPT) {
+            const int c = HF::PT0 + dt;
+            const uint8_t* cb = xb + chunk_base(c);
+            a[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[0][c & 1]));
+            b[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((CSA_LDS v2i*)(cb + pv_off[1][c & 1]));
           }
-        };
-        if (NB > 0) read_batch(0, ra[0], rb[0]);
-#pragma unroll
-        for (int bt = 0; bt < NB; ++bt) {
-          if (bt + 1 < NB) read_batch(bt + 1, ra[(bt + 1) & 1], rb[(bt + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int j = 0; j < PB; ++j) {
-            const int dt = bt * PB + j;
-            if (dt < HF::NPT) {
-              const v2i a0 = ra[bt & 1][j], a1 = rb[bt & 1][j];
-              const v8i a = (v8i){a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};
-              O[dt] = mfma_f8_128(a, pb, O[dt]);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      if (HF::NRT > 0) {
-        // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7); rope dim tile
-        // j = chunks CHNP + 2 j (+1)
-        v4i pbf[2];
+      };
+      if (NB > 0) read_batch(0, ra[0], rb[0]);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+      for (int bt = 0; bt < NB; ++bt) {
+        if (bt + 1 < NB) read_batch(bt + 1, ra[(bt + 1) & 1], rb[(bt + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pbf[u][e] = (int)pack2_bf16(pr[8 * u + 2 * e], pr[8 * u + 2 * e + 1]);
-        v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
-#pragma unroll
-        for (int j = 0; j < HF::NRT; ++j) {
-          const uint8_t* cb = xb + ((C::CHNP / 4 + (j >> 1)) * 16 + 2 * (j & 1)) * 256;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const v2i lo = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][0])));
-            const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][1])));
-            ya[j][u] = (v4i){lo[0], lo[1], hi[0], hi[1]};
+        for (int j = 0; j < PB; ++j) {
+          const int dt = bt * PB + j;
+          if (dt < HF::NPT) {
+            const v2i a0 = ra[bt & 1][j], a1 = rb[bt & 1][j];
+            const v8i a = (v8i){a0[0], a0[1], a1[0], a1[1], a0[0], a0[1], a1[0], a1[1]};
+            O[dt] = mfma_f8_128(a, pb, O[dt]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int j = 0; j < HF::NRT; ++j)
-            O[HF::NPT + j] = mfma_bf16_32(__builtin_bit_cast(v8bf, ya[j][u]), __builtin_bit_cast(v8bf, pbf[u]),
-                                          O[HF::NPT + j]);
       }
+    }
+    if (HF::NRT > 0) {
+      // rope, BF16: MFMA u covers keys 32 u + kappa(g, 0..7); rope dim tile
+      // j = chunks CHNP + 2 j (+1)
+      v4i pbf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pbf[u] = (v4i){pq[2 * u][2], pq[2 * u][3], pq[2 * u + 1][2], pq[2 * u + 1][3]};
+      v4i ya[HF::NRT > 0 ? HF::NRT : 1][2];
+#pragma unroll
+      for (int j = 0; j < HF::NRT; ++j) {
+        const uint8_t* cb = xb + ((C::CHNP / 4 + (j >> 1)) * 16 + 2 * (j & 1)) * 256;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const v2i lo = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][0])));
+          const v2i hi = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS v4s*)(cb + rp_off[u][1])));
+          ya[j][u] = (v4i){lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < HF::NRT; ++j)
+          O[HF::NPT + j] = mfma_bf16_32(__builtin_bit_cast(v8bf, ya[j][u]), __builtin_bit_cast(v8bf, pbf[u]),
+                                        O[HF::NPT + j]);
     }
   };
 
@@ -672,14 +680,35 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 #pragma unroll
     for (int st = 0; st < 4; ++st)
       tot[st] = ND == 2 ? pp[0][st] + pp[1][st] : (pp[0][st] + pp[1][st]) + (pp[ND - 2][st] + pp[ND - 1][st]);
+    v4i pq[4];
+    soft(it, tot, tile_swa, pq);
+    if constexpr (kSplitP) {
+      // this part's subtile of P to LDS, the other parts' back
+      px[wave * 64 + lane] = pq[DP];
+      lds_barrier();
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        if (st != DP) pq[st] = px[(st * HT + ht) * 64 + lane];
+    }
     __builtin_amdgcn_sched_barrier(0);
-    soft_pv(it, tot, xb, tile_swa);
+    pv(xb, pq);
     if (refill) issue_quads(nbuf, 2);
+  }
+  // the denominator: per part with split P (summed here over the parts in
+  // one order; the exchange buffer is free once the last tile's P is)
+  float L = sum_over_groups(l_run);
+  if constexpr (kSplitP) {
+    float* lx = reinterpret_cast<float*>(sx);
+    lx[wave * 64 + lane] = L;
+    lds_barrier();
+    float lp[ND];
+#pragma unroll
+    for (int dp = 0; dp < ND; ++dp) lp[dp] = lx[(dp * HT + ht) * 64 + lane];
+    L = (lp[0] + lp[1]) + (lp[2] + lp[3]);
   }
   if (!tile_ok) return;
 
   // ---- output of this part's dims (the softmax state is the same in every part)
-  const float L = sum_over_groups(l_run);
   const float M = m_run;
   const bool final_out = p.n_splits == 1;
   const float invL = (final_out && L > 0.0f) ? 1.0f / L : 0.0f;
@@ -721,6 +750,7 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf * C::TILE_BYTES];
   __shared__ int32_t desc[kAttnMaxSlots];
   __shared__ v4f sx[ND * HT * 4 * 64];   // partial score tiles, [wave][subtile][lane]
+  __shared__ v4i px[ND == 4 ? ND * HT * 64 : 1];   // four dim parts: each part's subtile of P, [wave][lane]
 
   // ---- which (query, head group, split).  Workgroups go to the 8 XCDs
   // round-robin by id.  With 8 or more queries, queries are spread over the
@@ -765,18 +795,18 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   __builtin_assume(wave >= 0 && wave < ND * HT);
   if constexpr (ND == 4) {
     if (wave >= 3 * HT)
-      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, wave);
+      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, px, wave);
     else if (wave >= 2 * HT)
-      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, wave);
+      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, px, wave);
     else if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, wave);
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, px, wave);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, wave);
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, px, wave);
   } else {
     if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, wave);
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, px, wave);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, wave);
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, px, wave);
   }
 }
 
