@@ -161,7 +161,7 @@ struct Block {
 
 template <int DN, int DR, int DP, int HT, int ND>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, uint8_t* xs0, int32_t* desc,
-                                          v4f* sx, v4i* px, int wave) {
+                                          v4f* sx, v2i* pxh, v2i* pxb, int wave) {
   using C = Cfg<DN, DR>;
   using HF = Part<DN, DR, ND, DP>;
   constexpr int D = DN + DR;
@@ -379,7 +379,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   const float sink2 = head_ok ? sink_raw * kLog2e : -__builtin_inff();
   float m_run = sink_here ? sink2 : -__builtin_inff();
   // (with split P the sink's share of the denominator is counted by part 0)
-  float l_run = (sink_here && g == 0 && sink2 > -__builtin_inff() && (ND != 4 || DP == 0)) ? 1.0f : 0.0f;
+  float l_run = (sink_here && g == 0 && sink2 > -__builtin_inff() && DP == 0) ? 1.0f : 0.0f;
   v4f O[HF::NO];
 #pragma unroll
   for (int i = 0; i < HF::NO; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -514,12 +514,13 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   };
   // online softmax and PV of tile `it` (tot: the exchanged score, summed over
   // the dim parts in the same order in every part)
-  // With four dim parts, each part exponentiates and packs the
-  // probabilities of one 16-key subtile only (the max still comes from the
-  // whole tile, so every part takes the same rescale decisions), and the
-  // parts swap their P through LDS; the denominator is kept per part and
-  // summed at the end.
-  constexpr bool kSplitP = ND == 4;
+  // Each dim part exponentiates and packs the probabilities of its own
+  // 16-key subtiles only (st % ND == dp; the max still comes from the whole
+  // tile, so every part takes the same rescale decisions), and the parts swap
+  // their P through LDS; the denominator is kept per part and summed at the
+  // end.
+  constexpr bool kSplitP = ND > 1;
+  constexpr int kOwnSt = 4 / ND;   // subtiles per part
   // online softmax of tile `it` (tot: the exchanged score, summed over the
   // dim parts in the same order in every part); P of subtile st, when this
   // part computes it, is pq[st] = (hi, lo E4M3 of p x kq; p as two BF16 pairs)
@@ -555,7 +556,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     float psum = 0.0f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      if (kSplitP && st != DP) continue;
+      if (kSplitP && st % ND != DP) continue;
       float pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -683,12 +684,28 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     v4i pq[4];
     soft(it, tot, tile_swa, pq);
     if constexpr (kSplitP) {
-      // this part's subtile of P to LDS, the other parts' back
-      px[wave * 64 + lane] = pq[DP];
+      // this part's subtiles of P to LDS (E4M3 hi/lo for every part; BF16,
+      // used by the rope dims, for the last part only), the other parts' back
+#pragma unroll
+      for (int j = 0; j < kOwnSt; ++j) {
+        const int st = DP + ND * j;
+        pxh[(wave * kOwnSt + j) * 64 + lane] = (v2i){pq[st][0], pq[st][1]};
+        if (!HF::LAST) pxb[((ht * (ND - 1) + DP) * kOwnSt + j) * 64 + lane] = (v2i){pq[st][2], pq[st][3]};
+      }
       lds_barrier();
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        if (st != DP) pq[st] = px[(st * HT + ht) * 64 + lane];
+      for (int st = 0; st < 4; ++st) {
+        const int dq = st % ND, j = st / ND;
+        if (dq == DP) continue;
+        const v2i hl = pxh[((dq * HT + ht) * kOwnSt + j) * 64 + lane];
+        pq[st][0] = hl[0];
+        pq[st][1] = hl[1];
+        if (HF::LAST) {
+          const v2i bf = pxb[((ht * (ND - 1) + dq) * kOwnSt + j) * 64 + lane];
+          pq[st][2] = bf[0];
+          pq[st][3] = bf[1];
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     pv(xb, pq);
@@ -704,7 +721,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     float lp[ND];
 #pragma unroll
     for (int dp = 0; dp < ND; ++dp) lp[dp] = lx[(dp * HT + ht) * 64 + lane];
-    L = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    L = ND == 2 ? lp[0] + lp[1] : (lp[0] + lp[1]) + (lp[ND - 2] + lp[ND - 1]);
   }
   if (!tile_ok) return;
 
@@ -750,7 +767,10 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf * C::TILE_BYTES];
   __shared__ int32_t desc[kAttnMaxSlots];
   __shared__ v4f sx[ND * HT * 4 * 64];   // partial score tiles, [wave][subtile][lane]
-  __shared__ v4i px[ND == 4 ? ND * HT * 64 : 1];   // four dim parts: each part's subtile of P, [wave][lane]
+  // each part's subtiles of P: E4M3 hi/lo [wave][subtile][lane]; BF16 of the
+  // parts other than the last [ht][part][subtile][lane]
+  __shared__ v2i pxh[ND * HT * (4 / ND) * 64];
+  __shared__ v2i pxb[(ND > 1 ? HT * (ND - 1) * (4 / ND) : 1) * 64];
 
   // ---- which (query, head group, split).  Workgroups go to the 8 XCDs
   // round-robin by id.  With 8 or more queries, queries are spread over the
@@ -795,18 +815,18 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   __builtin_assume(wave >= 0 && wave < ND * HT);
   if constexpr (ND == 4) {
     if (wave >= 3 * HT)
-      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, px, wave);
+      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
     else if (wave >= 2 * HT)
-      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, px, wave);
+      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
     else if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, px, wave);
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, px, wave);
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
   } else {
     if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, px, wave);
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, px, wave);
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
   }
 }
 
