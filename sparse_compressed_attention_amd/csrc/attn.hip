@@ -524,20 +524,9 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   // online softmax of tile `it` (tot: the exchanged score, summed over the
   // dim parts in the same order in every part); P of subtile st, when this
   // part computes it, is pq[st] = (hi, lo E4M3 of p x kq; p as two BF16 pairs)
-  auto soft = [&](int it, const v4f (&tot)[4], bool tile_swa, v4i (&pq)[4]) {
+  auto soft = [&](int it, const v4f (&tot)[4], float tmax, bool tile_swa, v4i (&pq)[4]) {
     const float msub = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // as subtracted in own_part
-    // -- lane: head h, keys 16 st + 4 g + i; sv = S - msub
-    float sv[16];
-    float tmax = -__builtin_inff();
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[4 * st + i] = tot[st][i];
-        tmax = fmaxf(tmax, tot[st][i]);
-      }
-    }
-    tmax = max_over_groups(tmax);
+    // -- lane: head h, keys 16 st + 4 g + i; tot = S - msub
     const bool m_inf = m_run == -__builtin_inff();
     const bool grow = m_inf ? (tmax > -__builtin_inff()) : (tmax > (float)kAttnTau);
     float delta = 0.0f;
@@ -560,7 +549,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
       float pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(sv[4 * st + i] - delta);   // exp2(-inf) = 0 for masked keys
+        pr[i] = __builtin_amdgcn_exp2f(tot[st][i] - delta);   // exp2(-inf) = 0 for masked keys
         psum += pr[i];
       }
       // nope operand bytes: hi of p x key-scale ratio x 2^(8 - tau), lo = the
@@ -672,17 +661,35 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     for (int st = 0; st < 4; ++st) sx_own[st * 64] = part[st];
     if (refill) issue_quads(nbuf, 1);
     lds_barrier();
-    v4f pp[ND][4];   // the parts' partials: own from registers, the others from LDS
-#pragma unroll
-    for (int dp = 0; dp < ND; ++dp)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) pp[dp][st] = dp == DP ? part[st] : sx_tile[(dp * HT * 4 + st) * 64];
+    // the scores of this part's own subtiles (four parts) or of all of them
+    // (two): the parts' partials (own from registers, the others from LDS)
+    // summed in one fixed order
+    constexpr bool kSplitMax = ND == 4;
     v4f tot[4];
+    float mloc = -__builtin_inff();
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-      tot[st] = ND == 2 ? pp[0][st] + pp[1][st] : (pp[0][st] + pp[1][st]) + (pp[ND - 2][st] + pp[ND - 1][st]);
+    for (int st = 0; st < 4; ++st) {
+      if (kSplitMax && st % ND != DP) continue;
+      v4f pp[ND];
+#pragma unroll
+      for (int dp = 0; dp < ND; ++dp) pp[dp] = dp == DP ? part[st] : sx_tile[(dp * HT * 4 + st) * 64];
+      tot[st] = ND == 2 ? pp[0] + pp[1] : (pp[0] + pp[1]) + (pp[ND - 2] + pp[ND - 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, tot[st][i]);
+    }
+    float tmax = max_over_groups(mloc);
+    if constexpr (kSplitMax) {
+      // the tile max over the parts, swapped through this part's slot of its
+      // own subtile DP, which no other part reads (one more barrier, for 36
+      // fewer adds)
+      *reinterpret_cast<float*>(sx_own + DP * 64) = tmax;
+      lds_barrier();
+#pragma unroll
+      for (int dp = 0; dp < ND; ++dp)
+        if (dp != DP) tmax = fmaxf(tmax, *reinterpret_cast<const float*>(sx_tile + (dp * HT * 4 + dp) * 64));
+    }
     v4i pq[4];
-    soft(it, tot, tile_swa, pq);
+    soft(it, tot, tmax, tile_swa, pq);
     if constexpr (kSplitP) {
       // this part's subtiles of P to LDS (E4M3 hi/lo for every part; BF16,
       // used by the rope dims, for the last part only), the other parts' back
