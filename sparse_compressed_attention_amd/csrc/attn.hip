@@ -414,12 +414,14 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   auto qk = [&](const uint8_t* xq) {
     // -- partial scores over this part's dims: four 16-key subtiles; the
     //    operands of the next step are read before the MFMAs of this one
+    // (no branch on the head tile: a tile beyond H has zero q rows, and the
+    // branch would make the compiler clear the accumulators with moves)
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       acc[st] = (v4f){0.f, 0.f, 0.f, 0.f};
       racc[st] = acc[st];
     }
-    if (tile_ok) {
+    {
       constexpr int NSTEP = HF::FB + (HF::COMB ? 1 : 0);
       auto read_step = [&](int step, v8i (&x)[4]) {
 #pragma unroll
