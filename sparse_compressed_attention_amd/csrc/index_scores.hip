@@ -34,6 +34,39 @@ namespace {
 // v_max first)
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
 
+// Weighted ReLU of one 16-entry group's MFMA outputs over this lane's 16
+// heads (heads 16 ht + 4 g + i of entry r), as two FMA chains.
+__device__ __forceinline__ float wrelu16(const v4f (&a)[4], const v4f (&w)[4]) {
+  float s0 = w[0][0] * relu(a[0][0]);
+  float s1 = w[2][0] * relu(a[2][0]);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    s0 = __builtin_fmaf(w[0][i], relu(a[0][i]), s0);
+    s1 = __builtin_fmaf(w[2][i], relu(a[2][i]), s1);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s0 = __builtin_fmaf(w[1][i], relu(a[1][i]), s0);
+    s1 = __builtin_fmaf(w[3][i], relu(a[3][i]), s1);
+  }
+  return s0 + s1;
+}
+
+// Sum over the four 16-lane groups of four values at once (a reduce-
+// scatter): x_u is this lane's partial of group u; lane group g gets group
+// g's total.  Three permlane swaps for four groups instead of two per group:
+// the 32-lane swaps leave groups 0, 1 in the lower half and 2, 3 in the
+// upper half (summed over the halves), the 16-lane swap the even and odd
+// groups in the even and odd rows.
+__device__ __forceinline__ float reduce4_scatter(float x0, float x1, float x2, float x3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x0), __float_as_int(x2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x1), __float_as_int(x3), false, false);
+  const float ya = __int_as_float(a[0]) + __int_as_float(a[1]);
+  const float yb = __int_as_float(b[0]) + __int_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_int(ya), __float_as_int(yb), false, false);
+  return __int_as_float(c[0]) + __int_as_float(c[1]);
+}
+
 // kWaves waves of kGroups groups of 16 entries: a workgroup scores
 // kWaves * kGroups * 16 consecutive entries of one query row.  kQLds: the
 // workgroup reads the query operand from memory once and hands it to its
@@ -42,6 +75,7 @@ template <int kWaves, int kGroups, int kOcc, bool kQLds>
 __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexParams p) {
   static_assert(!kQLds || kWaves >= 4, "four waves fill the shared query operand");
   static_assert(kGroups <= 64, "one page-id lane per group");
+  static_assert(kGroups % 4 == 0, "groups are reduced four at a time");
   constexpr int kWaveEntries = 16 * kGroups;
   constexpr int kChunk = kWaves * kWaveEntries;
   __shared__ v8i qs[kQLds ? 4 * 64 : 1];
@@ -140,7 +174,8 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   if (e_begin >= nv) return;
 
   // ---- software pipeline: the MFMAs of group u + 1 go out before the
-  // weighted ReLU of group u; the head sum runs as four independent chains
+  // weighted ReLU of group u; every four groups one reduce-scatter over the
+  // lane groups, after which lane (g, r) holds entry r of group 4 j + g
   float* out = p.scores + (size_t)t * p.ld;
   auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
 #pragma unroll
@@ -148,19 +183,18 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
       acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});   // rows of absent heads are zero
   };
   v4f acc[2][4];
+  float xg[4];
   mfmas(kb[0], acc[0]);
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) {
     if (u + 1 < kGroups) mfmas(kb[u + 1], acc[(u + 1) & 1]);
-    float pp[4];
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const v4f a = acc[u & 1][ht];
-      pp[ht] = wv[ht][0] * relu(a[0]) + wv[ht][1] * relu(a[1]) + (wv[ht][2] * relu(a[2]) + wv[ht][3] * relu(a[3]));
+    xg[u & 3] = wrelu16(acc[u & 1], wv);
+    if ((u & 3) == 3) {
+      const float tot = reduce4_scatter(xg[0], xg[1], xg[2], xg[3]);
+      const int ug = u - 3 + g;
+      const int e = e_begin + 16 * ug + r;
+      if (e < e_end) out[e] = ((ok_mask >> ug) & 1u) ? tot : -__builtin_inff();
     }
-    const float part = sum_over_groups((pp[0] + pp[1]) + (pp[2] + pp[3]));
-    const int e = e_begin + 16 * u + r;
-    if (g == 0 && e < e_end) out[e] = ((ok_mask >> u) & 1u) ? part : -__builtin_inff();
   }
 }
 
@@ -179,6 +213,7 @@ constexpr int kMqGroups = 16;
 constexpr int kMqChunk = 16 * kMqGroups;
 constexpr int kMqGpw = kMqGroups / kMqQ;    // groups loaded per wave per chunk
 static_assert(kMqGroups % kMqQ == 0, "groups split evenly over the waves");
+static_assert(kMqGroups % 4 == 0, "groups are reduced four at a time");
 
 __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexParams p, int n_split) {
   __shared__ __attribute__((aligned(16))) v8i ks[2][kMqGroups * 64];
@@ -302,8 +337,10 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
 #pragma unroll
       for (int w = 0; w < kMqQ; ++w) ok_mask |= okw[b][w];
       const int e_end = min(nv_own, e0 + kMqChunk);
-      // MFMAs of group u + 1 before the weighted ReLU of group u
+      // MFMAs of group u + 1 before the weighted ReLU of group u; one
+      // reduce-scatter per four groups (as in the one-query kernel)
       v4f acc[2][4];
+      float xg[4];
       v8i kb = ks[b][lane];
       mfmas(kb, acc[0]);
 #pragma unroll
@@ -312,15 +349,13 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
           kb = ks[b][(u + 1) * 64 + lane];
           mfmas(kb, acc[(u + 1) & 1]);
         }
-        float pp[4];
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
-          const v4f a = acc[u & 1][ht];
-          pp[ht] = wv[ht][0] * relu(a[0]) + wv[ht][1] * relu(a[1]) + (wv[ht][2] * relu(a[2]) + wv[ht][3] * relu(a[3]));
+        xg[u & 3] = wrelu16(acc[u & 1], wv);
+        if ((u & 3) == 3) {
+          const float tot = reduce4_scatter(xg[0], xg[1], xg[2], xg[3]);
+          const int ug = u - 3 + g;
+          const int e = e0 + 16 * ug + r;
+          if (e < e_end) out[e] = ((ok_mask >> ug) & 1u) ? tot : -__builtin_inff();
         }
-        const float part = sum_over_groups((pp[0] + pp[1]) + (pp[2] + pp[3]));
-        const int e = e0 + 16 * u + r;
-        if (g == 0 && e < e_end) out[e] = ((ok_mask >> u) & 1u) ? part : -__builtin_inff();
       }
     }
     if (more) store_keys(b ^ 1, kl, okbits);
