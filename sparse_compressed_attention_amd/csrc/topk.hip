@@ -207,8 +207,9 @@ __device__ void emit_selected(const uint32_t (&key)[SEG], uint32_t valid, const 
   }
 }
 
+// (at most 64 VGPRs, so that four 512-thread workgroups share a CU)
 template <int BLOCK, int SEG>
-__global__ __launch_bounds__(BLOCK) void topk_chunk_kernel(TopkParams p) {
+__global__ __launch_bounds__(BLOCK, 6) void topk_chunk_kernel(TopkParams p) {
   __shared__ TopkShared<BLOCK> sh;
   const int t = blockIdx.x / p.n_chunks;
   const int ch = blockIdx.x - t * p.n_chunks;
