@@ -10,7 +10,8 @@ check it against the pages by eye.
 Sources (cited by page title and section):
   [Audit]   "DSV4 Audit -- Decode Repetition + Precision / Tensor-Core Plan"
             (both revisions): A3 (visible range of compressed blocks, SWA /
-            compressed overlap), B1 (FP8_E4M3 nope dims + BF16 rope dims),
+            compressed overlap), A4 (inverse RoPE of the attention output
+            at the query position), B1 (FP8_E4M3 nope dims + BF16 rope dims),
             B2 (indexer scoring einsum 'tnd,cd->tnc', weighted-ReLU MQA
             logits, top-k with no global lock).
   [Roadmap] "ROADMAP -- Stage E and the path to a runnable model": E1 (paged
@@ -30,5 +31,5 @@ pure-Python brute force on tiny inputs.
 from .codecs import e4m3_decode, bf16_decode  # noqa: F401
 from .csa import (  # noqa: F401
     n_visible, index_scores, topk_select, key_rows, attend, run_decode_path,
-    run_attention, merge_by_lse, dequant_entries, entry_rows,
+    run_attention, merge_by_lse, dequant_entries, entry_rows, inverse_rope,
 )

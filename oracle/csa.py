@@ -242,3 +242,33 @@ def run_decode_path(wl, queries=None):
         ls_.append(lse)
     return dict(queries=ts, scores=scores, topk=np.stack(sels), o=np.stack(os_),
                 lse=np.stack(ls_))
+
+
+# --------------------------------------------------------------------------
+# After step 4: inverse RoPE of the output's rope dims
+# --------------------------------------------------------------------------
+def inverse_rope(o: np.ndarray, pos: int, d_nope: int, theta: float) -> np.ndarray:
+    """The attention output with its rope dims rotated back by RoPE(-pos).
+
+    [Audit] A4: the attention output is de-rotated at the query's own
+    position (not the compressed entries' positions) by the rotation with the
+    negated angle, which turns the absolute positions carried by the summed
+    latents into relative ones.  Readings (the pages give no formula): the
+    rope dims are the last D_rope dims (nope first); they pair up as
+    consecutive dims (2i, 2i + 1) of the rope part, taken as the real and
+    imaginary part of one complex number; pair i turns at frequency
+    theta^(-2i / D_rope), the usual rotary schedule with base theta.  The
+    forward rotation at position p multiplies pair i by exp(+1j p f_i), so the
+    inverse multiplies it by exp(-1j p f_i).  The nope dims are unchanged.
+    `o` is [..., D] (any leading shape).
+    """
+    o = np.array(o, dtype=np.float64, copy=True)
+    d_rope = o.shape[-1] - d_nope
+    freq = float(theta) ** (-2.0 * np.arange(d_rope // 2) / d_rope)
+    angle = -float(pos) * freq
+    c, s = np.cos(angle), np.sin(angle)
+    x = o[..., d_nope::2].copy()
+    y = o[..., d_nope + 1::2].copy()
+    o[..., d_nope::2] = x * c - y * s
+    o[..., d_nope + 1::2] = x * s + y * c
+    return o
