@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle's CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="device copies of the inputs (0 = enough for 1 GB)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured graph (csa_graph_*) instead of issuing its calls")
+    ap.add_argument("--inv-rope-theta", type=float, default=0.0,
+                    help="base of the inverse-RoPE epilogue on the output's rope dims (0 = off)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to calibrate HBM byte counters")
     return ap.parse_args()
@@ -159,7 +163,7 @@ def measured_traffic(workload, name):
 
 
 # --------------------------------------------------------------- CPU oracle leg
-def cpu_baseline(wl, gpu_res, seconds, is_prefill):
+def cpu_baseline(wl, gpu_res, seconds, is_prefill, inv_rope_theta=0.0):
     import numpy as np
     import oracle
     from tests import parity as P
@@ -181,6 +185,8 @@ def cpu_baseline(wl, gpu_res, seconds, is_prefill):
         else:
             o_ref, l_ref = oracle.run_attention(wl, None, queries=[t])
             o_ref, l_ref = o_ref[0], l_ref[0]
+        if inv_rope_theta:
+            o_ref = oracle.inverse_rope(o_ref, int(wl.q_pos[t]), wl.spec.D_nope, inv_rope_theta)
         done.append(t)
         errs.append(P.check_attention(gpu_res["o"][t], gpu_res["lse"][t], o_ref, l_ref))
         if time.perf_counter() - t0 > seconds:
@@ -224,7 +230,9 @@ def main():
     d0 = to_device(wl, dev)
     footprint = sum(t.numel() * t.element_size() for t in vars(d0).values() if isinstance(t, torch.Tensor))
     copies = args.copies or int(min(256, max(2, math.ceil((1 << 30) / max(footprint, 1)))))
-    paths = [make_path(d0)] + [make_path(to_device(wl, dev)) for _ in range(copies - 1)]
+    theta = args.inv_rope_theta
+    paths = [make_path(d0, inv_rope_theta=theta)] + [make_path(to_device(wl, dev), inv_rope_theta=theta)
+                                                     for _ in range(copies - 1)]
     del d0
     stages = paths[0].stage_names
     stream = torch.cuda.current_stream()
@@ -234,6 +242,11 @@ def main():
     for i in range(args.warmup):
         paths[i % copies].run(st)
     torch.cuda.synchronize()
+    graphs = [csa.StepGraph(p) for p in paths] if args.graph else None
+    if graphs:
+        for i in range(args.warmup):
+            graphs[i % copies].replay(st)
+        torch.cuda.synchronize()
 
     K = args.steps
     # Timed region 1, the headline: K whole steps back to back, nothing else
@@ -244,8 +257,12 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_begin.record(stream)
-    for i in range(K):
-        paths[i % copies].run(st)
+    if graphs:
+        for i in range(K):
+            graphs[i % copies].replay(st)
+    else:
+        for i in range(K):
+            paths[i % copies].run(st)
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -265,6 +282,22 @@ def main():
         torch.cuda.synchronize()
         per_stage.append(ea.elapsed_time(eb) / K)
     ms_per_step = wall * 1e3 / K
+    latency = None
+    if graphs:
+        # Single-step latency, the quantity graph replay is meant to cut: one
+        # step issued and waited for, as when every decode step depends on
+        # the previous one's output.  Median over 50 steps each way.
+        def one_step(fn):
+            ts = []
+            for i in range(50):
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                fn(i % copies)
+                torch.cuda.synchronize()
+                ts.append((time.perf_counter() - t1) * 1e6)
+            return round(float(np.median(ts)), 1)
+        latency = dict(eager_us=one_step(lambda i: paths[i].run(st)),
+                       graph_us=one_step(lambda i: graphs[i].replay(st)))
     n_items = wl.T
     value = n_items / (ms_per_step * 1e-3)
 
@@ -287,7 +320,8 @@ def main():
         n_gpus=1, steps=K, warmup=args.warmup, ms_per_step=round(ms_per_step, 5),
         higher_is_better=True, scaling="weak", vs_baseline=None, dtype="fp8", data="synthetic",
         config=dict(workload=f"{name}: {WORKLOADS[name]}", queries_per_step=n_items, input_copies=copies,
-                    gpu_ms_per_step=round(gpu_step, 5)),
+                    gpu_ms_per_step=round(gpu_step, 5), launch="graph replay" if graphs else "eager calls",
+                    inv_rope_theta=theta or None, synced_step_latency=latency),
         roofline=roof,
         kernels=kernels,
     )
@@ -298,7 +332,7 @@ def main():
         if getattr(last, "topk", None) is not None:
             res["topk"] = last.topk.cpu().numpy()
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, res, args.cpu_seconds, wl.spec.kind == "prefill")
+        out["cpu_baseline"] = cpu_baseline(wl, res, args.cpu_seconds, wl.spec.kind == "prefill", theta)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -43,8 +43,9 @@ def to_device(wl, device="cuda") -> SimpleNamespace:
     return d
 
 
-def make_path(d, csa=None):
-    """DecodePath (decode workloads) or PrefillPath (prefill chunk)."""
+def make_path(d, csa=None, inv_rope_theta=0.0):
+    """DecodePath (decode workloads) or PrefillPath (prefill chunk); a
+    nonzero inv_rope_theta turns on the inverse-RoPE epilogue."""
     if csa is None:
         import sparse_compressed_attention_amd as csa  # noqa: PLC0415
     s = d.spec
@@ -53,8 +54,8 @@ def make_path(d, csa=None):
         swa = csa.SwaRing(d.swa_nope, d.swa_rope, d.swa_scale, d.swa_pos)
         return csa.DecodePath(cache=cache, swa=swa, q=d.q, q_pos=d.q_pos, sink=d.sink, softmax_scale=s.sigma,
                               k=s.k, q_idx=d.q_idx, q_idx_scale=d.q_idx_scale, w=d.w, k_idx=d.k_idx,
-                              k_idx_scale=d.k_idx_scale)
+                              k_idx_scale=d.k_idx_scale, inv_rope_theta=inv_rope_theta)
     return csa.PrefillPath(cache=cache, seq=0, q=d.q, q_pos=d.q_pos, sink=d.sink, softmax_scale=s.sigma, k=s.k,
                            W=s.W, swa_nope=d.swa_nope, swa_rope=d.swa_rope, swa_scale=d.swa_scale,
                            swa_first_pos=d.swa_first_pos, q_idx=d.q_idx, q_idx_scale=d.q_idx_scale, w=d.w,
-                           k_idx=d.k_idx, k_idx_scale=d.k_idx_scale)
+                           k_idx=d.k_idx, k_idx_scale=d.k_idx_scale, inv_rope_theta=inv_rope_theta)

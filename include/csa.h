@@ -7,12 +7,14 @@
  *   csa_topk          causal top-k over those scores      (step 2)
  *   csa_decode_attn   gather + sink attention, decode     (steps 3+4)
  *   csa_prefill_attn  gather + sink attention, prefill    (steps 3+4)
+ * and graph capture/replay of a whole step (csa_graph_*).
  *
  * Sources (page title and section):
  *   [Audit]   "DSV4 Audit -- Decode Repetition + Precision / Tensor-Core
  *             Plan": A3 (visible compressed blocks; SWA/compressed overlap;
- *             "5. Gather KV"), B1 (FP8_E4M3 nope dims + BF16 rope dims fed
- *             to the MMA without dequantisation), B2 (weighted-ReLU MQA
+ *             "5. Gather KV"), A4 (inverse RoPE of the attention output),
+ *             B1 (FP8_E4M3 nope dims + BF16 rope dims fed to the MMA
+ *             without dequantisation), B2 (weighted-ReLU MQA
  *             indexer logits; top-k with no global lock).
  *   [Roadmap] "ROADMAP -- Stage E and the path to a runnable model": E1
  *             (paged FP8 cache + block table + stored scale; gathers of
@@ -20,7 +22,7 @@
  *             (launch returns a code, errors by peek-at-last-error, no
  *             device sync; attention returns (o, lse)), E5 (batch folded
  *             into the grid), E7 (indexer top-k), E8 (prefill spread over
- *             many workgroups).
+ *             many workgroups), E9 (graph capture of the decode step).
  *   [README]  "DSV4 Inference Kernel": Architecture (CSA m=4, HCA m'=128,
  *             latent (T, 512) shared by all 128 heads, sink weights merge
  *             the sparse and SWA attention).
@@ -163,6 +165,15 @@ int csa_topk(const float* scores, int64_t ld_scores, const int32_t* n_visible,
  *     out[t][h][:] = sum_j exp(S_j - M) x_j / den       (all D dims, BF16)
  *     lse[t][h]    = M + ln(den)                        (natural log)
  * No key and sink = -inf gives out = 0, lse = -inf.
+ * Inverse RoPE ([Audit] A4: the attention output is rotated back by
+ * RoPE(-pos) at the query's own position, which turns the absolute
+ * positions carried by the summed latents into relative ones): when
+ * inv_rope_theta > 0, the rope dims of out (dims D_nope + 2i and
+ * D_nope + 2i + 1, i < D_rope / 2) are rotated before the BF16 store:
+ *     a_i = -q_pos[t] * inv_rope_theta^(-2i / D_rope)
+ *     (x, y) -> (x cos a_i - y sin a_i, x sin a_i + y cos a_i)
+ * inv_rope_theta == 0 leaves out as defined above; lse is not affected.
+ * A negative or non-finite inv_rope_theta is CSA_ERR_INVALID_ARG.
  *   q [.][H][D] BF16 with row stride q_stride (elements between tokens,
  *   >= H*D, multiple of 8), 16-byte aligned; sink [H] float; out [.][H][D]
  *   BF16 contiguous; lse [.][H] float or NULL.
@@ -188,7 +199,7 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride,
                     const int32_t* topk_idx, int32_t k,
                     const csa_swa_ring* swa, const int32_t* q_pos,
                     const float* sink, float softmax_scale,
-                    int32_t B, int32_t H,
+                    float inv_rope_theta, int32_t B, int32_t H,
                     uint16_t* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -204,9 +215,40 @@ int csa_prefill_attn(const uint16_t* q, int64_t q_stride,
                      const uint8_t* swa_nope, const uint16_t* swa_rope,
                      float swa_scale, int32_t swa_first_pos, int32_t swa_len,
                      int32_t W, const int32_t* q_pos, int32_t T,
-                     const float* sink, float softmax_scale, int32_t H,
+                     const float* sink, float softmax_scale,
+                     float inv_rope_theta, int32_t H,
                      uint16_t* out, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Graph capture of a whole step ([Roadmap] E9: once the decode step is
+ * free of synchronisation, capture it once and replay it, removing the host
+ * launch overhead; no allocation on the hot path) -------------------------
+ * None of the calls above allocates, synchronises or reads a host value
+ * back, so a step (e.g. csa_index_scores -> csa_topk -> csa_decode_attn)
+ * can be recorded once and replayed with one launch:
+ *   csa_graph_capture_begin(s);  ...the step's calls on stream s...;
+ *   csa_graph_capture_end(s, &g);  then csa_graph_launch(g, any_stream)
+ * per step, and csa_graph_destroy(g) at the end.
+ * The graph keeps the device pointers, sizes and scalars of the captured
+ * calls: a replay reads the CURRENT contents of the same buffers (new q,
+ * new cache rows, new positions), but shapes, pointers, k, W and scales
+ * are fixed.  Host structs (csa_latent_cache, csa_swa_ring) are read only
+ * during capture.  Buffers must outlive the graph.
+ *   begin: `stream` must be a created stream (not NULL) that is not
+ *          already capturing (CSA_ERR_INVALID_ARG); capture is thread-local,
+ *          so only this thread's work on `stream` is recorded.
+ *   end:   ends the capture and instantiates it; *graph = NULL and
+ *          CSA_ERR_LAUNCH if the capture was invalidated.
+ *   launch: enqueues one replay on `stream` (NULL = default stream); replays
+ *          on one stream run in order, and replays of one graph must not
+ *          overlap on different streams (they share buffers).
+ * The handle is owned by the caller and freed by csa_graph_destroy (NULL
+ * is a no-op). */
+typedef struct csa_graph csa_graph;
+int csa_graph_capture_begin(void* stream);
+int csa_graph_capture_end(void* stream, csa_graph** graph);
+int csa_graph_launch(const csa_graph* graph, void* stream);
+void csa_graph_destroy(csa_graph* graph);
 
 /* Text of a status code (static storage). */
 const char* csa_status_string(int code);

@@ -20,6 +20,7 @@ __all__ = [
     "CsaError", "LatentCache", "SwaRing", "DecodePath", "PrefillPath", "library_path", "load_library",
     "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "csa_attn_workspace_size",
     "csa_decode_attn", "csa_prefill_attn", "csa_status_string", "csa_version",
+    "csa_graph_capture_begin", "csa_graph_capture_end", "csa_graph_launch", "csa_graph_destroy", "StepGraph",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -71,15 +72,23 @@ def load_library():
     lib.csa_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.csa_attn_workspace_size.restype = sz
     lib.csa_decode_attn.argtypes = [vp, i64, ctypes.POINTER(_LatentCacheC), vp, i32, ctypes.POINTER(_SwaRingC),
-                                    vp, vp, f32, i32, i32, vp, vp, vp, sz, vp]
+                                    vp, vp, f32, f32, i32, i32, vp, vp, vp, sz, vp]
     lib.csa_decode_attn.restype = ctypes.c_int
     lib.csa_prefill_attn.argtypes = [vp, i64, ctypes.POINTER(_LatentCacheC), i32, vp, i32, vp, vp, f32, i32, i32,
-                                     i32, vp, i32, vp, f32, i32, vp, vp, vp, sz, vp]
+                                     i32, vp, i32, vp, f32, f32, i32, vp, vp, vp, sz, vp]
     lib.csa_prefill_attn.restype = ctypes.c_int
     lib.csa_status_string.argtypes = [ctypes.c_int]
     lib.csa_status_string.restype = ctypes.c_char_p
     lib.csa_version.argtypes = []
     lib.csa_version.restype = ctypes.c_int
+    lib.csa_graph_capture_begin.argtypes = [vp]
+    lib.csa_graph_capture_begin.restype = ctypes.c_int
+    lib.csa_graph_capture_end.argtypes = [vp, ctypes.POINTER(vp)]
+    lib.csa_graph_capture_end.restype = ctypes.c_int
+    lib.csa_graph_launch.argtypes = [vp, vp]
+    lib.csa_graph_launch.restype = ctypes.c_int
+    lib.csa_graph_destroy.argtypes = [vp]
+    lib.csa_graph_destroy.restype = None
     _LIB = lib
     return lib
 
@@ -227,7 +236,7 @@ def csa_attn_workspace_size(n_queries: int, H: int, D_nope: int, D_rope: int, ma
 
 
 def csa_decode_attn(q, cache: LatentCache, topk_idx, k, swa: SwaRing, q_pos, sink, softmax_scale, out,
-                    lse=None, workspace=None, stream=None):
+                    lse=None, workspace=None, stream=None, inv_rope_theta=0.0):
     _need(q, "q", _B16, 3, contiguous=False)
     _need(q_pos, "q_pos", _I32, 1)
     _need(sink, "sink", _F32, 1)
@@ -243,12 +252,13 @@ def csa_decode_attn(q, cache: LatentCache, topk_idx, k, swa: SwaRing, q_pos, sin
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load_library().csa_decode_attn(
         _ptr(q), q.stride(0), ctypes.byref(cc), _ptr(topk_idx), int(k), ctypes.byref(sc), _ptr(q_pos), _ptr(sink),
-        float(softmax_scale), B, H, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+        float(softmax_scale), float(inv_rope_theta), B, H, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream))
     _check("csa_decode_attn", rc)
 
 
 def csa_prefill_attn(q, cache: LatentCache, seq, topk_idx, k, swa_nope, swa_rope, swa_scale, swa_first_pos, W,
-                     q_pos, sink, softmax_scale, out, lse=None, workspace=None, stream=None):
+                     q_pos, sink, softmax_scale, out, lse=None, workspace=None, stream=None, inv_rope_theta=0.0):
     _need(q, "q", _B16, 3, contiguous=False)
     _need(q_pos, "q_pos", _I32, 1)
     _need(sink, "sink", _F32, 1)
@@ -267,7 +277,8 @@ def csa_prefill_attn(q, cache: LatentCache, seq, topk_idx, k, swa_nope, swa_rope
     rc = load_library().csa_prefill_attn(
         _ptr(q), q.stride(0), ctypes.byref(cc), int(seq), _ptr(topk_idx), int(k), _ptr(swa_nope), _ptr(swa_rope),
         float(swa_scale), int(swa_first_pos), swa_nope.shape[0], int(W), _ptr(q_pos), T, _ptr(sink),
-        float(softmax_scale), H, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+        float(softmax_scale), float(inv_rope_theta), H, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream))
     _check("csa_prefill_attn", rc)
 
 
@@ -306,8 +317,9 @@ class DecodePath(_Path):
     visible compressed entry."""
 
     def __init__(self, *, cache: LatentCache, swa: SwaRing, q, q_pos, sink, softmax_scale, k,
-                 q_idx=None, q_idx_scale=1.0, w=None, k_idx=None, k_idx_scale=1.0):
+                 q_idx=None, q_idx_scale=1.0, w=None, k_idx=None, k_idx_scale=1.0, inv_rope_theta=0.0):
         dev = q.device
+        self.inv_rope_theta = float(inv_rope_theta)
         self.cache, self.swa, self.q, self.q_pos, self.sink = cache, swa, q, q_pos, sink
         self.softmax_scale, self.k = float(softmax_scale), int(k)
         self.q_idx, self.q_idx_scale, self.w, self.k_idx, self.k_idx_scale = q_idx, q_idx_scale, w, k_idx, k_idx_scale
@@ -356,7 +368,8 @@ class DecodePath(_Path):
         aw = 0 if self.attn_ws is None else self.attn_ws.numel()
         plan.append(("csa_decode_attn", (
             _ptr(self.q), self.q.stride(0), ctypes.byref(self._cc), _ptr(self.topk), self.k, ctypes.byref(self._sc),
-            _ptr(self.q_pos), _ptr(self.sink), self.softmax_scale, B, H, _ptr(self.out), _ptr(self.lse),
+            _ptr(self.q_pos), _ptr(self.sink), self.softmax_scale, self.inv_rope_theta, B, H, _ptr(self.out),
+            _ptr(self.lse),
             _ptr(self.attn_ws), aw)))
         return plan
 
@@ -368,8 +381,9 @@ class PrefillPath(_Path):
     stage_names = ("index_scores", "topk", "prefill_attn")
 
     def __init__(self, *, cache: LatentCache, seq, q, q_pos, sink, softmax_scale, k, W, swa_nope, swa_rope,
-                 swa_scale, swa_first_pos, q_idx, q_idx_scale, w, k_idx, k_idx_scale):
+                 swa_scale, swa_first_pos, q_idx, q_idx_scale, w, k_idx, k_idx_scale, inv_rope_theta=0.0):
         dev = q.device
+        self.inv_rope_theta = float(inv_rope_theta)
         self.cache, self.seq, self.q, self.q_pos, self.sink = cache, int(seq), q, q_pos, sink
         self.softmax_scale, self.k, self.W = float(softmax_scale), int(k), int(W)
         self.swa_nope, self.swa_rope, self.swa_scale, self.swa_first_pos = swa_nope, swa_rope, swa_scale, swa_first_pos
@@ -414,6 +428,68 @@ class PrefillPath(_Path):
             ("csa_prefill_attn", (
                 _ptr(self.q), self.q.stride(0), ctypes.byref(self._cc), self.seq, _ptr(self.topk), self.k,
                 _ptr(self.swa_nope), _ptr(self.swa_rope), float(self.swa_scale), int(self.swa_first_pos),
-                self.swa_nope.shape[0], self.W, _ptr(self.q_pos), T, _ptr(self.sink), self.softmax_scale, H,
+                self.swa_nope.shape[0], self.W, _ptr(self.q_pos), T, _ptr(self.sink), self.softmax_scale,
+                self.inv_rope_theta, H,
                 _ptr(self.out), _ptr(self.lse), _ptr(self.attn_ws), aw)),
         ]
+
+
+# ---------------------------------------------------------------- graph replay
+def csa_graph_capture_begin(stream) -> None:
+    _check("csa_graph_capture_begin", load_library().csa_graph_capture_begin(_stream(stream)))
+
+
+def csa_graph_capture_end(stream) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check("csa_graph_capture_end", load_library().csa_graph_capture_end(_stream(stream), ctypes.byref(h)))
+    return h
+
+
+def csa_graph_launch(graph: ctypes.c_void_p, stream=None) -> None:
+    _check("csa_graph_launch", load_library().csa_graph_launch(graph, _stream(stream)))
+
+
+def csa_graph_destroy(graph: ctypes.c_void_p) -> None:
+    load_library().csa_graph_destroy(graph)
+
+
+class StepGraph:
+    """One step of a DecodePath / PrefillPath recorded once with the library's
+    graph calls and replayed with a single launch.  A replay reads the current
+    contents of the path's buffers (refreshed q, positions, cache rows) and
+    writes path.out / path.lse; shapes and pointers are those of the capture."""
+
+    def __init__(self, path: "_Path"):
+        self.path = path
+        dev = path.out.device
+        cur = torch.cuda.current_stream(dev)
+        side = torch.cuda.Stream(device=dev)   # default priority
+        side.wait_stream(cur)
+        csa_graph_capture_begin(side)
+        try:
+            path.run(stream=side)
+        except BaseException:
+            h = ctypes.c_void_p()
+            load_library().csa_graph_capture_end(_stream(side), ctypes.byref(h))
+            if h.value:
+                csa_graph_destroy(h)
+            raise
+        self._h = csa_graph_capture_end(side)
+        cur.wait_stream(side)
+
+    def replay(self, stream=None):
+        if self._h is None:
+            raise RuntimeError("graph already destroyed")
+        csa_graph_launch(self._h, stream)
+        return self.path.out, self.path.lse
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            csa_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass

@@ -738,13 +738,41 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   const float M = m_run;
   const bool final_out = p.n_splits == 1;
   const float invL = (final_out && L > 0.0f) ? 1.0f / L : 0.0f;
+  // inverse RoPE of the rope dims at the query position, when this
+  // workgroup writes the final output (split outputs are rotated by the
+  // merge).  Lane i < DR / 2 forms the rotation of pair i; every lane then
+  // fetches the two pairs of each of its rope tiles (dims 4g .. 4g + 3 of
+  // tile j are pairs 8j + 2g and 8j + 2g + 1), outside the head branch so
+  // that every lane takes part in the swaps.
+  float2 rcs[HF::NRT > 0 ? HF::NRT : 1][2];
+  const bool rot = HF::LAST && final_out && p.inv_rope;
+  if constexpr (HF::NRT > 0) {
+    if (rot) {
+      const float2 own = lane < DR / 2 ? inv_rope_cs(bk.pos, lane, DR, p.rope_log2_theta) : make_float2(1.0f, 0.0f);
+#pragma unroll
+      for (int j = 0; j < HF::NRT; ++j)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int pr = 8 * j + 2 * g + e;
+          rcs[j][e] = make_float2(__shfl(own.x, pr, 64), __shfl(own.y, pr, 64));
+        }
+    }
+  }
   if (head_ok) {
 #pragma unroll
     for (int j = 0; j < HF::NO; ++j) {
       const bool nope = j < HF::NPT;
       const float unit = nope ? p.nope_unit : 1.0f;
       const int dim = nope ? 16 * (HF::PT0 + j) + 4 * g : DN + 16 * (j - HF::NPT) + 4 * g;
-      const v4f v = O[j] * unit;
+      v4f v = O[j] * unit;
+      if constexpr (HF::NRT > 0) {
+        if (!nope && rot) {
+          const int jr = j >= HF::NPT ? j - HF::NPT : 0;
+          const float2 a = rotate2(v[0], v[1], rcs[jr][0]);
+          const float2 b = rotate2(v[2], v[3], rcs[jr][1]);
+          v = (v4f){a.x, a.y, b.x, b.y};
+        }
+      }
       if (final_out) {
         const v2i pk = (v2i){(int)pack2_bf16(v[0] * invL, v[1] * invL), (int)pack2_bf16(v[2] * invL, v[3] * invL)};
         *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + dim) = pk;
@@ -900,6 +928,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
       for (int j = 0; j < 4; ++j) acc += v[j] * wgt[half][s + j];
     }
     for (; s < used; ++s) acc += *reinterpret_cast<const v4f*>(row + s * pstride + d0) * wgt[half][s];
+    if (d0 >= p.D_nope && p.inv_rope) {
+      // inverse RoPE of rope pairs (d0 - D_nope) / 2 and the next one
+      const int pr = (d0 - p.D_nope) >> 1;
+      const float2 a = rotate2(acc[0], acc[1], inv_rope_cs(pos, pr, p.D_rope, p.rope_log2_theta));
+      const float2 b = rotate2(acc[2], acc[3], inv_rope_cs(pos, pr + 1, p.D_rope, p.rope_log2_theta));
+      acc = (v4f){a.x, a.y, b.x, b.y};
+    }
     *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + d0) =
         (v2i){(int)pack2_bf16(acc[0] * invL, acc[1] * invL), (int)pack2_bf16(acc[2] * invL, acc[3] * invL)};
   }

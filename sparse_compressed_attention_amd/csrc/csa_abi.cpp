@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <new>
 
 #include "csa.h"
 #include "csa_internal.h"
@@ -111,7 +112,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_LAUN
 
 extern "C" {
 
-int csa_version(void) { return 100; }
+int csa_version(void) { return 110; }
 
 const char* csa_status_string(int code) {
   switch (code) {
@@ -206,6 +207,13 @@ size_t csa_attn_workspace_size(int32_t n_queries, int32_t H, int32_t D_nope, int
   return pl.ws_bytes;
 }
 
+// inverse RoPE base: 0 (no rotation) or a finite value > 0
+static bool rope_theta_ok(float theta) { return theta == 0.0f || (std::isfinite(theta) && theta > 0.0f); }
+static void set_inv_rope(AttnParams& p, float theta) {
+  p.inv_rope = theta > 0.0f ? 1 : 0;
+  p.rope_log2_theta = theta > 0.0f ? std::log2((double)theta) : 0.0;
+}
+
 static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t workspace_bytes, void* stream) {
   const float smax = std::max(p.lat_scale, p.swa_scale);
   const float pmul = std::ldexp(1.0f, 8 - kAttnTau);
@@ -239,7 +247,7 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
 
 int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache, const int32_t* topk_idx,
                     int32_t k, const csa_swa_ring* swa, const int32_t* q_pos, const float* sink,
-                    float softmax_scale, int32_t B, int32_t H, uint16_t* out, float* lse, void* workspace,
+                    float softmax_scale, float inv_rope_theta, int32_t B, int32_t H, uint16_t* out, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 1) return CSA_ERR_INVALID_ARG;
   if (B == 0) return CSA_OK;
@@ -252,6 +260,7 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache*
   if (q_stride < (int64_t)H * D || q_stride % 8) return CSA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale) || !(swa->nope_scale > 0.0f) || !std::isfinite(swa->nope_scale))
     return CSA_ERR_INVALID_ARG;
+  if (!rope_theta_ok(inv_rope_theta)) return CSA_ERR_INVALID_ARG;
   if (swa->W < 1 || swa->W > 1024) return CSA_ERR_UNSUPPORTED;
   if ((int64_t)B * swa->W >= (int64_t)1 << 30) return CSA_ERR_UNSUPPORTED;
   if (topk_idx && (k < 0 || k > kTopkMaxK)) return CSA_ERR_UNSUPPORTED;
@@ -273,6 +282,7 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache*
   p.lat_scale = cache->nope_scale;
   p.swa_scale = swa->nope_scale;
   p.sm_scale = softmax_scale;
+  set_inv_rope(p, inv_rope_theta);
   p.num_pages = cache->num_pages;
   p.page_size = cache->page_size;
   p.max_pages = cache->max_pages;
@@ -291,7 +301,8 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache*
 int csa_prefill_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache, int32_t seq,
                      const int32_t* topk_idx, int32_t k, const uint8_t* swa_nope, const uint16_t* swa_rope,
                      float swa_scale, int32_t swa_first_pos, int32_t swa_len, int32_t W, const int32_t* q_pos,
-                     int32_t T, const float* sink, float softmax_scale, int32_t H, uint16_t* out, float* lse,
+                     int32_t T, const float* sink, float softmax_scale, float inv_rope_theta, int32_t H,
+                     uint16_t* out, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream) {
   if (T < 0 || H < 1 || seq < 0 || swa_len < 0) return CSA_ERR_INVALID_ARG;
   if (T == 0) return CSA_OK;
@@ -304,7 +315,7 @@ int csa_prefill_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache
   if (!aligned16(q) || !aligned16(out)) return CSA_ERR_INVALID_ARG;
   const int D = cache->D_nope + cache->D_rope;
   if (q_stride < (int64_t)H * D || q_stride % 8) return CSA_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return CSA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale) || !rope_theta_ok(inv_rope_theta)) return CSA_ERR_INVALID_ARG;
   if (swa_len > 0 && (!(swa_scale > 0.0f) || !std::isfinite(swa_scale))) return CSA_ERR_INVALID_ARG;
   if (W < 1 || W > 1024) return CSA_ERR_UNSUPPORTED;
   if (swa_len >= (1 << 30)) return CSA_ERR_UNSUPPORTED;
@@ -327,6 +338,7 @@ int csa_prefill_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache
   p.lat_scale = cache->nope_scale;
   p.swa_scale = swa_len > 0 ? swa_scale : cache->nope_scale;
   p.sm_scale = softmax_scale;
+  set_inv_rope(p, inv_rope_theta);
   p.num_pages = cache->num_pages;
   p.page_size = cache->page_size;
   p.max_pages = cache->max_pages;
@@ -342,6 +354,62 @@ int csa_prefill_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache
   p.D_rope = cache->D_rope;
   const int64_t max_slots = (topk_idx ? (int64_t)k : (int64_t)cache->max_pages * cache->page_size) + W;
   return run_attn(p, max_slots, workspace, workspace_bytes, stream);
+}
+
+// ---- graph capture of a whole step ("ROADMAP -- Stage E ...", E9: a
+// decode step free of synchronisation is captured once and replayed; the
+// calls above never allocate or synchronise, so a sequence of them can be
+// recorded as it is) --------------------------------------------------------
+struct csa_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+int csa_graph_capture_begin(void* stream) {
+  if (!stream) return CSA_ERR_INVALID_ARG;   // the legacy default stream cannot be captured
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &st) != hipSuccess) return CSA_ERR_INVALID_ARG;
+  if (st != hipStreamCaptureStatusNone) return CSA_ERR_INVALID_ARG;
+  return hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal) == hipSuccess
+             ? CSA_OK
+             : CSA_ERR_LAUNCH;
+}
+
+int csa_graph_capture_end(void* stream, csa_graph** graph) {
+  if (!stream || !graph) return CSA_ERR_INVALID_ARG;
+  *graph = nullptr;
+  hipGraph_t g = nullptr;
+  if (hipStreamEndCapture((hipStream_t)stream, &g) != hipSuccess || !g) {
+    (void)hipGetLastError();   // a failed capture leaves its error behind; it is reported here
+    if (g) (void)hipGraphDestroy(g);
+    return CSA_ERR_LAUNCH;
+  }
+  hipGraphExec_t ex = nullptr;
+  if (hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) != hipSuccess || !ex) {
+    (void)hipGetLastError();
+    (void)hipGraphDestroy(g);
+    return CSA_ERR_LAUNCH;
+  }
+  csa_graph* h = new (std::nothrow) csa_graph{g, ex};
+  if (!h) {
+    (void)hipGraphExecDestroy(ex);
+    (void)hipGraphDestroy(g);
+    return CSA_ERR_LAUNCH;
+  }
+  *graph = h;
+  return CSA_OK;
+}
+
+int csa_graph_launch(const csa_graph* graph, void* stream) {
+  if (!graph) return CSA_ERR_INVALID_ARG;
+  return hipGraphLaunch(graph->exec, (hipStream_t)stream) == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+void csa_graph_destroy(csa_graph* graph) {
+  if (!graph) return;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  delete graph;
 }
 
 }  // extern "C"

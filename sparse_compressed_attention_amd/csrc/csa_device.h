@@ -132,6 +132,27 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse rotary embedding of the output's rope dims ("DSV4 Audit -- Decode
+// Repetition + Precision / Tensor-Core Plan", A4: the attention output is
+// rotated by RoPE(-pos) at the query position, which turns the absolute
+// positions carried by the summed keys into relative ones).  Rope dims pair
+// up as (2i, 2i + 1) with frequency theta^(-2i / d_rope); the returned
+// (cos, sin) are those of the angle -pos * theta^(-2i / d_rope).  The angle is
+// formed and reduced to [-pi, pi] in FP64, so that the FP32 sin/cos keep
+// their accuracy at positions near 2^31.
+__device__ __forceinline__ float2 inv_rope_cs(int pos, int pair, int d_rope, double log2_theta) {
+  const double f = exp2(-(double)(2 * pair) / (double)d_rope * log2_theta);
+  double a = (double)pos * f;
+  a -= 6.283185307179586 * rint(a * 0.15915494309189535);
+  float s, c;
+  sincosf(-(float)a, &s, &c);
+  return make_float2(c, s);
+}
+// (x, y) rotated by the angle whose cosine and sine are cs.
+__device__ __forceinline__ float2 rotate2(float x, float y, float2 cs) {
+  return make_float2(x * cs.x - y * cs.y, x * cs.y + y * cs.x);
+}
+
 __device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 
 }  // namespace csa

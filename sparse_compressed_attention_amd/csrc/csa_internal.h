@@ -63,6 +63,10 @@ struct AttnParams {
   // per key source (key scale / max scale * 2^(8 - tau)); value unit of the
   // FP8 accumulator (max scale / 2^(8 - tau))
   float sm_log2, pscale_lat, pscale_swa, nope_unit;
+  // inverse RoPE of the output's rope dims at the query position (inv_rope
+  // != 0) with base 2^rope_log2_theta
+  double rope_log2_theta;
+  int inv_rope;
   // entry / page_size == (entry * ps_magic) >> ps_shift for 0 <= entry < 2^31
   uint64_t ps_magic;
   int ps_shift;

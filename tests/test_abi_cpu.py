@@ -78,9 +78,9 @@ def test_null_arguments_rejected_without_launch(lib):
     assert rc == -1
     rc = lib.csa_topk(None, 64, None, 4, 16, None, None, 0, None)
     assert rc == -1
-    rc = lib.csa_decode_attn(None, 512, None, None, 16, None, None, None, 1.0, 2, 128, None, None, None, 0, None)
+    rc = lib.csa_decode_attn(None, 512, None, None, 16, None, None, None, 1.0, 0.0, 2, 128, None, None, None, 0, None)
     assert rc == -1
-    rc = lib.csa_prefill_attn(None, 512, None, 0, None, 16, None, None, 1.0, 0, 0, 128, None, 4, None, 1.0, 128,
+    rc = lib.csa_prefill_attn(None, 512, None, 0, None, 16, None, None, 1.0, 0, 0, 128, None, 4, None, 1.0, 0.0, 128,
                               None, None, None, 0, None)
     assert rc == -1
     # zero-sized work is a no-op success
@@ -106,31 +106,47 @@ def test_unsupported_shapes_rejected(lib):
     assert rc == -4      # long rows need the workspace
     cache = csa._LatentCacheC(1 << 20, 1 << 20, 1.0, 1 << 20, 1 << 20, 2, 8, 64, 4, 100, 64, 4)
     ring = csa._SwaRingC(1 << 20, 1 << 20, 1.0, 1 << 20, 128)
-    rc = lib.csa_decode_attn(fake, 512, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake, 1.0, 2, 128,
+    rc = lib.csa_decode_attn(fake, 512, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake, 1.0, 0.0, 2, 128,
                              fake, None, None, 0, None)
     assert rc == -2      # D_nope 100 has no kernel
     cache.D_nope = 448
     ring.W = 4096
-    rc = lib.csa_decode_attn(fake, 512 * 128, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake, 1.0, 2, 128,
+    rc = lib.csa_decode_attn(fake, 512 * 128, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake, 1.0, 0.0, 2, 128,
                              fake, None, None, 0, None)
     assert rc == -2      # window too large
     ring.W = 128
-    rc = lib.csa_decode_attn(fake, 100, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake, 1.0, 2, 128,
+    rc = lib.csa_decode_attn(fake, 100, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake, 1.0, 0.0, 2, 128,
                              fake, None, None, 0, None)
     assert rc == -1      # q stride below H*D
     misaligned = ctypes.c_void_p((1 << 20) + 4)
     rc = lib.csa_decode_attn(misaligned, 512 * 128, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake,
-                             1.0, 2, 128, fake, None, None, 0, None)
+                             1.0, 0.0, 2, 128, fake, None, None, 0, None)
     assert rc == -1      # misaligned q
     rc = lib.csa_decode_attn(fake, 512 * 128, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake,
-                             1.0, 3, 128, fake, None, None, 0, None)
+                             1.0, 0.0, 3, 128, fake, None, None, 0, None)
     assert rc == -1      # more queries than cached sequences
     rc = lib.csa_prefill_attn(fake, 512 * 128, ctypes.byref(cache), 2, fake, 16, fake, fake, 1.0, 0, 8, 128, fake,
-                              4, fake, 1.0, 128, fake, None, None, 0, None)
+                              4, fake, 1.0, 0.0, 128, fake, None, None, 0, None)
     assert rc == -1      # prefill sequence beyond the page table
+    for theta in (-10000.0, float("nan"), float("inf")):
+        rc = lib.csa_decode_attn(fake, 512 * 128, ctypes.byref(cache), fake, 16, ctypes.byref(ring), fake, fake,
+                                 1.0, theta, 2, 128, fake, None, None, 0, None)
+        assert rc == -1  # inverse-RoPE base must be 0 (off) or finite and > 0
+        rc = lib.csa_prefill_attn(fake, 512 * 128, ctypes.byref(cache), 0, fake, 16, fake, fake, 1.0, 0, 8, 128,
+                                  fake, 4, fake, 1.0, theta, 128, fake, None, None, 0, None)
+        assert rc == -1
 
 
 def test_binding_refuses_cpu_tensors(lib):
     import torch
     with pytest.raises(ValueError):
         csa.csa_topk(torch.zeros(4, 64), torch.zeros(4, dtype=torch.int32), 8, torch.zeros(4, 8, dtype=torch.int32))
+
+
+def test_graph_calls_reject_null_handles_without_gpu_work(lib):
+    # argument checks run before any HIP call
+    h = ctypes.c_void_p()
+    assert lib.csa_graph_capture_begin(None) == -1       # the legacy default stream cannot be captured
+    assert lib.csa_graph_capture_end(None, ctypes.byref(h)) == -1
+    assert lib.csa_graph_launch(None, None) == -1
+    lib.csa_graph_destroy(None)                          # no-op

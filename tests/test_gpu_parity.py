@@ -31,9 +31,9 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(wl):
+def run_gpu(wl, inv_rope_theta=0.0):
     d = to_device(wl, "cuda")
-    path = make_path(d)
+    path = make_path(d, inv_rope_theta=inv_rope_theta)
     out, lse = path.run()
     torch.cuda.synchronize()
     res = dict(o=out.float().cpu().numpy().astype(np.float64), lse=lse.cpu().numpy().astype(np.float64))
@@ -44,10 +44,11 @@ def run_gpu(wl):
     return res
 
 
-def check_full(wl, queries=None, exact_topk_expected=None):
-    """Run the whole path on the GPU and compare the listed queries."""
+def check_full(wl, queries=None, exact_topk_expected=None, inv_rope_theta=0.0):
+    """Run the whole path on the GPU and compare the listed queries (with the
+    inverse-RoPE epilogue when inv_rope_theta > 0)."""
     s = wl.spec
-    res = run_gpu(wl)
+    res = run_gpu(wl, inv_rope_theta)
     qs = list(range(wl.T)) if queries is None else list(queries)
     worst = (0.0, 1.0)
     sc_err = 0.0
@@ -65,9 +66,11 @@ def check_full(wl, queries=None, exact_topk_expected=None):
         else:
             sel = None
         o_ref, l_ref = P.reference_attention_on(wl, t, sel)
+        if inv_rope_theta:
+            o_ref = oracle.inverse_rope(o_ref, int(wl.q_pos[t]), s.D_nope, inv_rope_theta)
         err, cos = P.check_attention(res["o"][t], res["lse"][t], o_ref, l_ref)
         worst = (max(worst[0], err), min(worst[1], cos))
-    say(f"  {s.name}: {len(qs)} queries, max|err| {worst[0]:.3e}, min cos {worst[1]:.6f}, "
+    say(f"  {s.name}{' (inverse RoPE)' if inv_rope_theta else ''}: {len(qs)} queries, max|err| {worst[0]:.3e}, min cos {worst[1]:.6f}, "
         f"score err {sc_err:.2e} of row max, exact top-k sets {exact}/{len(qs)}")
     return res
 
@@ -155,6 +158,35 @@ def test_single_tile_key_range():
     say("case decode single tile (k 16, window 32)")
     spec = ci.small_spec(name="small_one_tile", ctx_lens=[2000, 640], k=16, W=32)
     check_full(ci.generate(spec, seed=116))
+
+
+# --------------------------------------------------------------- inverse RoPE
+# The epilogue runs in three places: the attention kernel's last dim part
+# when a workgroup writes the final output (four parts: decode batches that
+# fill the GPU; two parts: prefill), and the split merge (few queries).
+@pytest.mark.parametrize("case", ["c0_merge", "small_merge", "prefill_two_parts", "tiny_prefill_two_parts"])
+def test_inverse_rope_epilogue(case):
+    say(f"case inverse RoPE {case}")
+    if case == "c0_merge":
+        wl, qs = ci.make_config("c0"), None
+    elif case == "small_merge":
+        wl, qs = ci.generate(ci.small_spec(shuffle_pages=True), seed=121), None
+    elif case == "prefill_two_parts":
+        spec = ci.Spec(name="prefill_160", kind="prefill", ctx_lens=[6000], T_prefill=160)
+        wl, qs = ci.generate(spec, seed=122), [0, 1, 63, 64, 100, 159]
+    else:
+        spec = ci.Spec(name="tiny_prefill_260", kind="prefill", ctx_lens=[2000], T_prefill=260, H=8, D_nope=48,
+                       D_rope=16, H_I=4, D_I=32, k=16, W=32, page_size=16)
+        wl, qs = ci.generate(spec, seed=123), [0, 130, 259]
+    check_full(wl, queries=qs, inv_rope_theta=10000.0)
+
+
+@pytest.mark.parametrize("name,queries,theta", [("c2", [0, 13, 63], 10000.0), ("c3_csa", [0, 3], 1e6)])
+def test_inverse_rope_full_size(name, queries, theta):
+    # c2: 64 queries fill the GPU, so the four-part kernel writes the output;
+    # c3: positions near 2^19, where the angle needs its FP64 reduction
+    say(f"case inverse RoPE full size {name}")
+    check_full(ci.make_config(name), queries=queries, inv_rope_theta=theta)
 
 
 def test_ring_permutation_invariance_gpu():
