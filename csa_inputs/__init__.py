@@ -37,6 +37,36 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_pack(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Store x [..., D] (D a multiple of 32) in the OCP MX FP4 format:
+    E2M1 codes two per byte (element 2j in the low nibble) [..., D/2] and
+    one E8M0 scale byte per block of 32 [..., D/32].  The block scale is
+    2^(floor(log2 amax) - 2) (the MX rule: the largest E2M1 exponent is 2);
+    elements are rounded to the nearest E2M1 value, ties to the even code,
+    and saturate at 6."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    assert D % 32 == 0
+    blk = x.reshape(x.shape[:-1] + (D // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(amax)                       # amax = f * 2^ex, f in [0.5, 1)
+    e = np.where(amax > 0, ex - 1 - 2, -127).clip(-127, 127)
+    y = blk / np.ldexp(1.0, e)[..., None]
+    a = np.minimum(np.abs(y), 6.0)
+    hi = np.searchsorted(_E2M1_GRID, a, side="left").clip(0, 7)
+    lo = (hi - 1).clip(0, 7)
+    dlo = a - _E2M1_GRID[lo]
+    dhi = _E2M1_GRID[hi] - a
+    code = np.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo)
+    code = code | (((y < 0) & (code > 0)).astype(np.int64) << 3)
+    code = code.reshape(x.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def per_tensor_scale(x: np.ndarray, unit: bool) -> float:
     if unit:
         return 1.0
@@ -62,6 +92,7 @@ class Spec:
     shuffle_pages: bool = False
     unit_scale: bool = False       # values already on the E4M3 grid (scale 1)
     with_indexer: bool = True      # False for the HCA layer (no indexer inputs)
+    mxfp4: bool = False            # also store the indexer q/k in MXFP4 (same draws)
     # prefill only: number of query tokens at the end of the single sequence
     T_prefill: int = 0
     # decode: position of each sequence's query (default ctx_len - 1)
@@ -88,6 +119,11 @@ class Workload:
     w: Optional[np.ndarray] = None         # f32 [T][H_I]
     k_idx: Optional[np.ndarray] = None     # u8 [P][ps][D_I]
     k_idx_scale: float = 1.0
+    # the same indexer draws in MXFP4 (spec.mxfp4): E2M1 pairs + E8M0 scales
+    q_idx4: Optional[np.ndarray] = None    # u8 [T][H_I][D_I/2]
+    q_idx4_sc: Optional[np.ndarray] = None # u8 [T][H_I][D_I/32]
+    k_idx4: Optional[np.ndarray] = None    # u8 [P][ps][D_I/2]
+    k_idx4_sc: Optional[np.ndarray] = None # u8 [P][ps][D_I/32]
     # compressed latent cache
     lat_nope: np.ndarray = None            # u8 [P][ps][D_nope]
     lat_rope: np.ndarray = None            # u16 [P][ps][D_rope]
@@ -158,11 +194,15 @@ def generate(spec: Spec, seed: int) -> Workload:
         qi = _draw_normal(rng, (T, s.H_I, s.D_I))
         wl.q_idx_scale = per_tensor_scale(qi, s.unit_scale)
         wl.q_idx = e4m3_bytes(qi, wl.q_idx_scale)
+        if s.mxfp4:
+            wl.q_idx4, wl.q_idx4_sc = mxfp4_pack(qi)
         del qi
         wl.w = rng.random((T, s.H_I), dtype=np.float32)
         ki = _draw_normal(rng, (n_entries, s.D_I))
         wl.k_idx_scale = per_tensor_scale(ki, s.unit_scale)
         ki_b = e4m3_bytes(ki, wl.k_idx_scale)
+        if s.mxfp4:
+            ki4, ki4_sc = mxfp4_pack(ki)
         del ki
     # ---- compressed latents
     lat = _draw_normal(rng, (n_entries, s.D))
@@ -203,6 +243,9 @@ def generate(spec: Spec, seed: int) -> Workload:
     wl.lat_rope = np.zeros((P, ps, s.D_rope), dtype=np.uint16)
     if s.with_indexer:
         wl.k_idx = np.zeros((P, ps, s.D_I), dtype=np.uint8)
+        if s.mxfp4:
+            wl.k_idx4 = np.zeros((P, ps, s.D_I // 2), dtype=np.uint8)
+            wl.k_idx4_sc = np.zeros((P, ps, s.D_I // 32), dtype=np.uint8)
     logical = 0
     e0 = 0
     for b in range(B):
@@ -217,6 +260,9 @@ def generate(spec: Spec, seed: int) -> Workload:
             wl.lat_rope[phys, :cnt] = lat_r[lo:hi]
             if s.with_indexer:
                 wl.k_idx[phys, :cnt] = ki_b[lo:hi]
+                if s.mxfp4:
+                    wl.k_idx4[phys, :cnt] = ki4[lo:hi]
+                    wl.k_idx4_sc[phys, :cnt] = ki4_sc[lo:hi]
         e0 += int(n_comp[b])
     wl.page_table = page_table
     return wl
@@ -256,10 +302,15 @@ CONFIG_NAMES = ["c0", "c1", "c2", "c3_csa", "c3_hca", "c4"]
 _CONFIG_INDEX = {"c0": 0, "c1": 1, "c2": 2, "c3_csa": 3, "c3_hca": 3, "c4": 4}
 
 
-def make_config(name: str, seed: Optional[int] = None) -> Workload:
+def make_config(name: str, seed: Optional[int] = None, mxfp4: bool = False) -> Workload:
+    """One of the configurations; mxfp4 adds the MXFP4 copy of the indexer
+    inputs (from the same draws, so every other array is unchanged)."""
     if seed is None:
         seed = BASE_SEED + _CONFIG_INDEX[name] + (100 if name == "c3_hca" else 0)
-    return generate(spec_for(name), seed)
+    spec = spec_for(name)
+    if mxfp4:
+        spec = dataclasses.replace(spec, mxfp4=True)
+    return generate(spec, seed)
 
 
 def small_spec(name: str = "small", **kw) -> Spec:

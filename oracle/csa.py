@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import e4m3_decode, bf16_decode
+from .codecs import e4m3_decode, bf16_decode, mxfp4_decode
 
 
 # --------------------------------------------------------------------------
@@ -54,6 +54,29 @@ def sequence_index_keys(wl, b: int) -> np.ndarray:
     rows = entry_rows(wl.page_table[b], s.page_size, np.arange(int(wl.n_comp[b])))
     flat = wl.k_idx.reshape(-1, s.D_I)
     return e4m3_decode(flat[rows]) * float(wl.k_idx_scale)
+
+
+def sequence_index_keys_mxfp4(wl, b: int) -> np.ndarray:
+    """All stored MXFP4 indexer keys of sequence b, float64 [n_comp][D_I]."""
+    s = wl.spec
+    rows = entry_rows(wl.page_table[b], s.page_size, np.arange(int(wl.n_comp[b])))
+    return mxfp4_decode(wl.k_idx4.reshape(-1, s.D_I // 2)[rows], wl.k_idx4_sc.reshape(-1, s.D_I // 32)[rows])
+
+
+def index_scores_mxfp4(wl, t: int, keys: np.ndarray | None = None) -> np.ndarray:
+    """The indexer scores of index_scores() with q_idx and k_idx taken from
+    their MXFP4 copies ([Audit] B2: the QK of the indexer in FP4, as the
+    paper does; [Roadmap] E7: FP4 keys and queries with block scales decoded
+    by the hardware).  Same formula; only the stored values differ."""
+    s = wl.spec
+    b = int(wl.q_seq[t])
+    nv = n_visible(int(wl.q_pos[t]), s.m, int(wl.n_comp[b]))
+    if keys is None:
+        keys = sequence_index_keys_mxfp4(wl, b)
+    q = mxfp4_decode(wl.q_idx4[t], wl.q_idx4_sc[t])                  # [H_I][D_I]
+    logits = q @ keys[:nv].T
+    w = wl.w[t].astype(np.float64)
+    return w @ np.maximum(logits, 0.0)
 
 
 def index_scores(wl, t: int, keys: np.ndarray | None = None) -> np.ndarray:
