@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="device copies of the inputs (0 = enough for 1 GB)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured graph (csa_graph_*) instead of issuing its calls")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="indexer on MXFP4 inputs (csa_index_scores_mxfp4) instead of E4M3")
     ap.add_argument("--inv-rope-theta", type=float, default=0.0,
                     help="base of the inverse-RoPE epilogue on the output's rope dims (0 = off)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -82,10 +84,12 @@ def calibrate_copy(mib):
 
 
 # --------------------------------------------------------------- accounting
-def accounting(wl):
+def accounting(wl, mxfp4=False):
     """Algorithmic bytes and FLOPs per launch of each step: only what the
     method must move (visible index keys once, q_idx, w, scores written and
-    read back, selected + window latent rows once per query, q and o)."""
+    read back, selected + window latent rows once per query, q and o).  With
+    the MXFP4 indexer an index row is D_I / 2 code bytes + D_I / 32 scale
+    bytes instead of D_I E4M3 bytes."""
     import numpy as np
     s = wl.spec
     T = wl.T
@@ -104,12 +108,13 @@ def accounting(wl):
     row = s.D_nope + 2 * s.D_rope
     acc = {}
     if wl.q_idx is not None:
+        idx_row = s.D_I // 2 + s.D_I // 32 if mxfp4 else s.D_I
         if s.kind == "decode":
-            key_bytes = int(nv.sum()) * s.D_I
+            key_bytes = int(nv.sum()) * idx_row
         else:
-            key_bytes = int(nv.max()) * s.D_I     # one sequence: every key is read once per chunk
+            key_bytes = int(nv.max()) * idx_row   # one sequence: every key is read once per chunk
         acc["index_scores"] = dict(
-            bytes=key_bytes + T * s.H_I * (s.D_I + 4) + int(nv.sum()) * 4 + T * 4,
+            bytes=key_bytes + T * s.H_I * (idx_row + 4) + int(nv.sum()) * 4 + T * 4,
             flops=2.0 * s.H_I * s.D_I * float(nv.sum()))
         acc["topk"] = dict(bytes=int(nv.sum()) * 4 + T * s.k * 4 + T * 4, flops=0.0)
     keys = n_sel + n_win
@@ -178,10 +183,14 @@ def cpu_baseline(wl, gpu_res, seconds, is_prefill, inv_rope_theta=0.0):
     done = []
     errs = []
     t0 = time.perf_counter()
+    overlap = []
     for t in order:
         res = oracle.run_decode_path(wl, queries=[t]) if wl.q_idx is not None else None
         if res is not None:
             o_ref, l_ref = P.reference_attention_on(wl, t, gpu_res["topk"][t])
+            ref_set = set(int(i) for i in res["topk"][0] if i >= 0)
+            got = set(int(i) for i in gpu_res["topk"][t] if i >= 0)
+            overlap.append(len(ref_set & got) / max(1, len(ref_set)))
         else:
             o_ref, l_ref = oracle.run_attention(wl, None, queries=[t])
             o_ref, l_ref = o_ref[0], l_ref[0]
@@ -196,7 +205,9 @@ def cpu_baseline(wl, gpu_res, seconds, is_prefill, inv_rope_theta=0.0):
     return dict(value=round(len(done) / el, 3), unit=unit, cores=int(cores), kind="oracle",
                 sample=f"{len(done)} of {wl.T} queries (random order, seed 0), FP64 NumPy oracle, "
                        f"{el:.1f} s; its outputs also checked the GPU's: max|o-ref| "
-                       f"{max(e[0] for e in errs):.2e}, min per-head cos {min(e[1] for e in errs):.6f}")
+                       f"{max(e[0] for e in errs):.2e}, min per-head cos {min(e[1] for e in errs):.6f}"
+                       + (f"; GPU top-k vs the oracle's (E4M3-input) top-k: mean overlap {np.mean(overlap):.4f}"
+                          if overlap else ""))
 
 
 # --------------------------------------------------------------- main
@@ -225,14 +236,15 @@ def main():
     dev = "cuda:0"
     name = args.workload
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
-    wl = ci.make_config(name)
-    acc = accounting(wl)
+    wl = ci.make_config(name, mxfp4=args.mxfp4)
+    acc = accounting(wl, args.mxfp4)
     d0 = to_device(wl, dev)
     footprint = sum(t.numel() * t.element_size() for t in vars(d0).values() if isinstance(t, torch.Tensor))
     copies = args.copies or int(min(256, max(2, math.ceil((1 << 30) / max(footprint, 1)))))
     theta = args.inv_rope_theta
-    paths = [make_path(d0, inv_rope_theta=theta)] + [make_path(to_device(wl, dev), inv_rope_theta=theta)
-                                                     for _ in range(copies - 1)]
+    fp4 = args.mxfp4
+    paths = [make_path(d0, inv_rope_theta=theta, mxfp4=fp4)] + [
+        make_path(to_device(wl, dev), inv_rope_theta=theta, mxfp4=fp4) for _ in range(copies - 1)]
     del d0
     stages = paths[0].stage_names
     stream = torch.cuda.current_stream()
@@ -321,7 +333,8 @@ def main():
         higher_is_better=True, scaling="weak", vs_baseline=None, dtype="fp8", data="synthetic",
         config=dict(workload=f"{name}: {WORKLOADS[name]}", queries_per_step=n_items, input_copies=copies,
                     gpu_ms_per_step=round(gpu_step, 5), launch="graph replay" if graphs else "eager calls",
-                    inv_rope_theta=theta or None, synced_step_latency=latency),
+                    inv_rope_theta=theta or None, indexer="MXFP4" if fp4 else "E4M3",
+                    synced_step_latency=latency),
         roofline=roof,
         kernels=kernels,
     )

@@ -39,23 +39,31 @@ def to_device(wl, device="cuda") -> SimpleNamespace:
         d.k_idx = _t(wl.k_idx, device)
     else:
         d.q_idx = d.w = d.k_idx = None
+    d.q_idx4 = d.q_idx4_sc = d.k_idx4 = d.k_idx4_sc = None
+    if wl.q_idx4 is not None:
+        d.q_idx4, d.q_idx4_sc = _t(wl.q_idx4, device), _t(wl.q_idx4_sc, device)
+        d.k_idx4, d.k_idx4_sc = _t(wl.k_idx4, device), _t(wl.k_idx4_sc, device)
     d.q_idx_scale, d.k_idx_scale = float(wl.q_idx_scale), float(wl.k_idx_scale)
     return d
 
 
-def make_path(d, csa=None, inv_rope_theta=0.0):
+def make_path(d, csa=None, inv_rope_theta=0.0, mxfp4=False):
     """DecodePath (decode workloads) or PrefillPath (prefill chunk); a
-    nonzero inv_rope_theta turns on the inverse-RoPE epilogue."""
+    nonzero inv_rope_theta turns on the inverse-RoPE epilogue; mxfp4 feeds
+    the indexer the MXFP4 copy of its inputs."""
     if csa is None:
         import sparse_compressed_attention_amd as csa  # noqa: PLC0415
     s = d.spec
+    idx = dict(q_idx=d.q_idx, q_idx_scale=d.q_idx_scale, w=d.w, k_idx=d.k_idx, k_idx_scale=d.k_idx_scale)
+    if mxfp4:
+        if d.q_idx4 is None:
+            raise ValueError("the workload has no MXFP4 indexer inputs (generate it with mxfp4=True)")
+        idx.update(q_idx=d.q_idx4, k_idx=d.k_idx4, q_idx_sc=d.q_idx4_sc, k_idx_sc=d.k_idx4_sc)
     cache = csa.LatentCache(d.lat_nope, d.lat_rope, d.lat_scale, d.page_table, d.n_comp, s.m)
     if s.kind == "decode":
         swa = csa.SwaRing(d.swa_nope, d.swa_rope, d.swa_scale, d.swa_pos)
         return csa.DecodePath(cache=cache, swa=swa, q=d.q, q_pos=d.q_pos, sink=d.sink, softmax_scale=s.sigma,
-                              k=s.k, q_idx=d.q_idx, q_idx_scale=d.q_idx_scale, w=d.w, k_idx=d.k_idx,
-                              k_idx_scale=d.k_idx_scale, inv_rope_theta=inv_rope_theta)
+                              k=s.k, inv_rope_theta=inv_rope_theta, **idx)
     return csa.PrefillPath(cache=cache, seq=0, q=d.q, q_pos=d.q_pos, sink=d.sink, softmax_scale=s.sigma, k=s.k,
                            W=s.W, swa_nope=d.swa_nope, swa_rope=d.swa_rope, swa_scale=d.swa_scale,
-                           swa_first_pos=d.swa_first_pos, q_idx=d.q_idx, q_idx_scale=d.q_idx_scale, w=d.w,
-                           k_idx=d.k_idx, k_idx_scale=d.k_idx_scale, inv_rope_theta=inv_rope_theta)
+                           swa_first_pos=d.swa_first_pos, inv_rope_theta=inv_rope_theta, **idx)

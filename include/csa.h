@@ -4,6 +4,7 @@
  *
  * The path has four steps, exposed as four calls (plus workspace queries):
  *   csa_index_scores  lightning-indexer scores            (step 1)
+ *                     (csa_index_scores_mxfp4: FP4 operands)
  *   csa_topk          causal top-k over those scores      (step 2)
  *   csa_decode_attn   gather + sink attention, decode     (steps 3+4)
  *   csa_prefill_attn  gather + sink attention, prefill    (steps 3+4)
@@ -133,6 +134,33 @@ int csa_index_scores(const uint8_t* q_idx, float q_idx_scale, const float* w,
                      int32_t H_I, int32_t D_I, int32_t ratio_m,
                      float* scores, int64_t ld_scores, int32_t* n_visible,
                      void* stream);
+
+/* ---- Step 1, MXFP4 variant ([Audit] B2: the indexer QK on FP4 tensor
+ * units; [Roadmap] E7: FP4 indexer scoring) -------------------------------
+ * Same result definition and arguments as csa_index_scores, with q_idx and
+ * k_idx in the OCP MX FP4 format instead of E4M3 with a per-tensor scale:
+ *   q_idx    [T][H_I][D_I / 2] bytes, k_idx [num_pages][page_size][D_I / 2]
+ *            bytes (16-byte aligned): E2M1 codes, two per byte, element 2j
+ *            in bits 0-3 and element 2j + 1 in bits 4-7; code = sign bit 3,
+ *            exponent bits 2-1, mantissa bit 0 (values 0, 0.5, 1, 1.5, 2,
+ *            3, 4, 6 and their negatives);
+ *   q_idx_sc [T][H_I][D_I / 32], k_idx_sc [num_pages][page_size][D_I / 32]
+ *            bytes: E8M0 block scales, value 2^(byte - 127), one per block of
+ *            32 consecutive dims (byte 255 = NaN is not allowed).
+ * The real value of element d of a row is e2m1(code_d) * 2^(sc[d/32] - 127).
+ * Products are exact in FP32 and accumulate in FP32, so the scores equal
+ * the definition on the decoded values up to FP32 summation order.  The key
+ * scan reads D_I / 2 + D_I / 32 bytes per entry (68 at D_I = 128), about
+ * half of the E4M3 scan.  Errors as csa_index_scores (null scale arrays are
+ * CSA_ERR_INVALID_ARG). */
+int csa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_idx_sc, const float* w,
+                           const uint8_t* k_idx, const uint8_t* k_idx_sc,
+                           const int32_t* page_table, const int32_t* n_comp,
+                           int32_t num_pages, int32_t page_size, int32_t max_pages, int32_t B,
+                           const int32_t* q_pos, const int32_t* q_seq, int32_t T,
+                           int32_t H_I, int32_t D_I, int32_t ratio_m,
+                           float* scores, int64_t ld_scores, int32_t* n_visible,
+                           void* stream);
 
 /* ---- Step 2: causal top-k ([Audit] B2; [Roadmap] E7) ------------------
  * For each row t, selects the min(k, n_visible[t]) largest of

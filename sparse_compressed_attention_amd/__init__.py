@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "CsaError", "LatentCache", "SwaRing", "DecodePath", "PrefillPath", "library_path", "load_library",
-    "csa_index_scores", "csa_topk", "csa_topk_workspace_size", "csa_attn_workspace_size",
+    "csa_index_scores", "csa_index_scores_mxfp4", "csa_topk", "csa_topk_workspace_size", "csa_attn_workspace_size",
     "csa_decode_attn", "csa_prefill_attn", "csa_status_string", "csa_version",
     "csa_graph_capture_begin", "csa_graph_capture_end", "csa_graph_launch", "csa_graph_destroy", "StepGraph",
 ]
@@ -65,6 +65,9 @@ def load_library():
     lib.csa_index_scores.argtypes = [vp, f32, vp, vp, f32, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32,
                                      vp, i64, vp, vp]
     lib.csa_index_scores.restype = ctypes.c_int
+    lib.csa_index_scores_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32,
+                                           vp, i64, vp, vp]
+    lib.csa_index_scores_mxfp4.restype = ctypes.c_int
     lib.csa_topk_workspace_size.argtypes = [i32, i64, i32]
     lib.csa_topk_workspace_size.restype = sz
     lib.csa_topk.argtypes = [vp, i64, vp, i32, i32, vp, vp, sz, vp]
@@ -211,6 +214,36 @@ def csa_index_scores(q_idx, q_idx_scale, w, k_idx, k_idx_scale, page_table, n_co
     _check("csa_index_scores", rc)
 
 
+def csa_index_scores_mxfp4(q_idx, q_idx_sc, w, k_idx, k_idx_sc, page_table, n_comp, q_pos, q_seq, ratio_m,
+                           scores, n_visible, stream=None):
+    """MXFP4 indexer: q_idx [T][H_I][D_I/2] and k_idx [P][ps][D_I/2] packed
+    E2M1 bytes, q_idx_sc [T][H_I][D_I/32] and k_idx_sc [P][ps][D_I/32] E8M0."""
+    _need(q_idx, "q_idx", _U8, 3)
+    _need(q_idx_sc, "q_idx_sc", _U8, 3)
+    _need(w, "w", _F32, 2)
+    _need(k_idx, "k_idx", _U8, 3)
+    _need(k_idx_sc, "k_idx_sc", _U8, 3)
+    _need(page_table, "page_table", _I32, 2)
+    _need(n_comp, "n_comp", _I32, 1)
+    _need(q_pos, "q_pos", _I32, 1)
+    _need(q_seq, "q_seq", _I32, 1)
+    _need(scores, "scores", _F32, 2, contiguous=False)
+    _need(n_visible, "n_visible", _I32, 1)
+    if scores.stride(1) != 1:
+        raise ValueError("scores rows must be contiguous")
+    T, H_I, DH = q_idx.shape
+    D_I = 2 * DH
+    P, ps, dk = k_idx.shape
+    if (dk != DH or tuple(w.shape) != (T, H_I) or scores.shape[0] != T or D_I % 32
+            or tuple(q_idx_sc.shape) != (T, H_I, D_I // 32) or tuple(k_idx_sc.shape) != (P, ps, D_I // 32)):
+        raise ValueError("inconsistent MXFP4 indexer shapes")
+    rc = load_library().csa_index_scores_mxfp4(
+        _ptr(q_idx), _ptr(q_idx_sc), _ptr(w), _ptr(k_idx), _ptr(k_idx_sc), _ptr(page_table), _ptr(n_comp), P, ps,
+        page_table.shape[1], page_table.shape[0], _ptr(q_pos), _ptr(q_seq), T, H_I, D_I, int(ratio_m),
+        _ptr(scores), scores.stride(0), _ptr(n_visible), _stream(stream))
+    _check("csa_index_scores_mxfp4", rc)
+
+
 def csa_topk_workspace_size(T: int, ld_scores: int, k: int) -> int:
     return int(load_library().csa_topk_workspace_size(int(T), int(ld_scores), int(k)))
 
@@ -294,6 +327,24 @@ class _Path:
         lib = load_library()
         self._stages = [(getattr(lib, fn), fn, args) for fn, args in self._plan()]
 
+    def _index_stage(self):
+        """The indexer call of the step: E4M3 with per-tensor scales, or
+        MXFP4 when the block-scale tensors were given."""
+        T, H_I, DQ = self.q_idx.shape
+        P, ps, _ = self.k_idx.shape
+        pt = self.cache.page_table
+        tail = (_ptr(pt), _ptr(self.cache.n_comp), P, ps, pt.shape[1], pt.shape[0], _ptr(self.q_pos),
+                _ptr(self.q_seq), T, H_I)
+        if self.q_idx_sc is not None and self.k_idx_sc is not None:
+            _need(self.q_idx_sc, "q_idx_sc", _U8, 3)
+            _need(self.k_idx_sc, "k_idx_sc", _U8, 3)
+            return ("csa_index_scores_mxfp4", (
+                _ptr(self.q_idx), _ptr(self.q_idx_sc), _ptr(self.w), _ptr(self.k_idx), _ptr(self.k_idx_sc), *tail,
+                2 * DQ, int(self.cache.ratio_m), _ptr(self.scores), self.ld, _ptr(self.n_vis)))
+        return ("csa_index_scores", (
+            _ptr(self.q_idx), float(self.q_idx_scale), _ptr(self.w), _ptr(self.k_idx), float(self.k_idx_scale),
+            *tail, DQ, int(self.cache.ratio_m), _ptr(self.scores), self.ld, _ptr(self.n_vis)))
+
     def run_stage(self, i: int, stream=None):
         fn, name, args = self._stages[i]
         rc = fn(*args, _stream(stream))
@@ -317,9 +368,11 @@ class DecodePath(_Path):
     visible compressed entry."""
 
     def __init__(self, *, cache: LatentCache, swa: SwaRing, q, q_pos, sink, softmax_scale, k,
-                 q_idx=None, q_idx_scale=1.0, w=None, k_idx=None, k_idx_scale=1.0, inv_rope_theta=0.0):
+                 q_idx=None, q_idx_scale=1.0, w=None, k_idx=None, k_idx_scale=1.0, inv_rope_theta=0.0,
+                 q_idx_sc=None, k_idx_sc=None):
         dev = q.device
         self.inv_rope_theta = float(inv_rope_theta)
+        self.q_idx_sc, self.k_idx_sc = q_idx_sc, k_idx_sc   # both given: MXFP4 indexer inputs
         self.cache, self.swa, self.q, self.q_pos, self.sink = cache, swa, q, q_pos, sink
         self.softmax_scale, self.k = float(softmax_scale), int(k)
         self.q_idx, self.q_idx_scale, self.w, self.k_idx, self.k_idx_scale = q_idx, q_idx_scale, w, k_idx, k_idx_scale
@@ -354,14 +407,7 @@ class DecodePath(_Path):
             _need(self.q_idx, "q_idx", _U8, 3)
             _need(self.k_idx, "k_idx", _U8, 3)
             _need(self.w, "w", _F32, 2)
-            T, H_I, D_I = self.q_idx.shape
-            P, ps, _ = self.k_idx.shape
-            pt = self.cache.page_table
-            plan.append(("csa_index_scores", (
-                _ptr(self.q_idx), float(self.q_idx_scale), _ptr(self.w), _ptr(self.k_idx), float(self.k_idx_scale),
-                _ptr(pt), _ptr(self.cache.n_comp), P, ps, pt.shape[1], pt.shape[0], _ptr(self.q_pos),
-                _ptr(self.q_seq), T, H_I, D_I, int(self.cache.ratio_m), _ptr(self.scores), self.ld,
-                _ptr(self.n_vis))))
+            plan.append(self._index_stage())
             tw = 0 if self.topk_ws is None else self.topk_ws.numel()
             plan.append(("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), B, self.k, _ptr(self.topk),
                                       _ptr(self.topk_ws), tw)))
@@ -381,9 +427,11 @@ class PrefillPath(_Path):
     stage_names = ("index_scores", "topk", "prefill_attn")
 
     def __init__(self, *, cache: LatentCache, seq, q, q_pos, sink, softmax_scale, k, W, swa_nope, swa_rope,
-                 swa_scale, swa_first_pos, q_idx, q_idx_scale, w, k_idx, k_idx_scale, inv_rope_theta=0.0):
+                 swa_scale, swa_first_pos, q_idx, q_idx_scale, w, k_idx, k_idx_scale, inv_rope_theta=0.0,
+                 q_idx_sc=None, k_idx_sc=None):
         dev = q.device
         self.inv_rope_theta = float(inv_rope_theta)
+        self.q_idx_sc, self.k_idx_sc = q_idx_sc, k_idx_sc   # both given: MXFP4 indexer inputs
         self.cache, self.seq, self.q, self.q_pos, self.sink = cache, int(seq), q, q_pos, sink
         self.softmax_scale, self.k, self.W = float(softmax_scale), int(k), int(W)
         self.swa_nope, self.swa_rope, self.swa_scale, self.swa_first_pos = swa_nope, swa_rope, swa_scale, swa_first_pos
@@ -412,17 +460,10 @@ class PrefillPath(_Path):
         _need(self.w, "w", _F32, 2)
         _need(self.swa_nope, "swa_nope", _U8, 2)
         _need(self.swa_rope, "swa_rope", _B16, 2)
-        _, H_I, D_I = self.q_idx.shape
-        P, ps, _ = self.k_idx.shape
-        pt = self.cache.page_table
         tw = 0 if self.topk_ws is None else self.topk_ws.numel()
         aw = 0 if self.attn_ws is None else self.attn_ws.numel()
         return [
-            ("csa_index_scores", (
-                _ptr(self.q_idx), float(self.q_idx_scale), _ptr(self.w), _ptr(self.k_idx), float(self.k_idx_scale),
-                _ptr(pt), _ptr(self.cache.n_comp), P, ps, pt.shape[1], pt.shape[0], _ptr(self.q_pos),
-                _ptr(self.q_seq), T, H_I, D_I, int(self.cache.ratio_m), _ptr(self.scores), self.ld,
-                _ptr(self.n_vis))),
+            self._index_stage(),
             ("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), T, self.k, _ptr(self.topk),
                           _ptr(self.topk_ws), tw)),
             ("csa_prefill_attn", (

@@ -112,7 +112,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_LAUN
 
 extern "C" {
 
-int csa_version(void) { return 110; }
+int csa_version(void) { return 120; }
 
 const char* csa_status_string(int code) {
   switch (code) {
@@ -125,25 +125,17 @@ const char* csa_status_string(int code) {
   }
 }
 
-int csa_index_scores(const uint8_t* q_idx, float q_idx_scale, const float* w, const uint8_t* k_idx,
-                     float k_idx_scale, const int32_t* page_table, const int32_t* n_comp, int32_t num_pages,
-                     int32_t page_size, int32_t max_pages, int32_t B, const int32_t* q_pos, const int32_t* q_seq,
-                     int32_t T, int32_t H_I, int32_t D_I, int32_t ratio_m, float* scores, int64_t ld_scores,
-                     int32_t* n_visible, void* stream) {
-  if (T < 0) return CSA_ERR_INVALID_ARG;
-  if (T == 0) return CSA_OK;
-  if (!q_idx || !w || !k_idx || !page_table || !n_comp || !q_pos || !q_seq || !scores || !n_visible)
+// Checks and launch shared by the FP8 and MXFP4 indexer entry points.
+static int index_scores_common(IndexParams& p, const int32_t* page_table, const int32_t* n_comp, int32_t num_pages,
+                               int32_t page_size, int32_t max_pages, int32_t B, const int32_t* q_pos,
+                               const int32_t* q_seq, int32_t T, int32_t H_I, int32_t D_I, int32_t ratio_m,
+                               float* scores, int64_t ld_scores, int32_t* n_visible, void* stream) {
+  if (!p.q_idx || !p.w || !p.k_idx || !page_table || !n_comp || !q_pos || !q_seq || !scores || !n_visible)
     return CSA_ERR_INVALID_ARG;
-  if (!aligned16(q_idx) || !aligned16(k_idx)) return CSA_ERR_INVALID_ARG;
+  if (!aligned16(p.q_idx) || !aligned16(p.k_idx)) return CSA_ERR_INVALID_ARG;
   if (B < 1 || num_pages < 1 || page_size < 16 || page_size % 16 || max_pages < 1 || ratio_m < 1 || ld_scores < 1)
     return CSA_ERR_INVALID_ARG;
-  if (!(q_idx_scale > 0.0f) || !(k_idx_scale > 0.0f) || !std::isfinite(q_idx_scale) || !std::isfinite(k_idx_scale))
-    return CSA_ERR_INVALID_ARG;
   if (H_I < 1 || H_I > 64 || !(D_I == 32 || D_I == 64 || D_I == 96 || D_I == 128)) return CSA_ERR_UNSUPPORTED;
-  IndexParams p{};
-  p.q_idx = q_idx;
-  p.w = w;
-  p.k_idx = k_idx;
   p.page_table = page_table;
   p.n_comp = n_comp;
   p.q_pos = q_pos;
@@ -151,7 +143,6 @@ int csa_index_scores(const uint8_t* q_idx, float q_idx_scale, const float* w, co
   p.scores = scores;
   p.n_visible = n_visible;
   p.ld = ld_scores;
-  p.qk_scale = q_idx_scale * k_idx_scale;
   p.num_pages = num_pages;
   p.page_size = page_size;
   p.max_pages = max_pages;
@@ -164,6 +155,44 @@ int csa_index_scores(const uint8_t* q_idx, float q_idx_scale, const float* w, co
   if ((int64_t)T * ceil_div(std::min<int64_t>(ld_scores, (int64_t)max_pages * page_size), 256) >= ((int64_t)1 << 31))
     return CSA_ERR_UNSUPPORTED;
   return launch_status(launch_index_scores(p, (hipStream_t)stream));
+}
+
+int csa_index_scores(const uint8_t* q_idx, float q_idx_scale, const float* w, const uint8_t* k_idx,
+                     float k_idx_scale, const int32_t* page_table, const int32_t* n_comp, int32_t num_pages,
+                     int32_t page_size, int32_t max_pages, int32_t B, const int32_t* q_pos, const int32_t* q_seq,
+                     int32_t T, int32_t H_I, int32_t D_I, int32_t ratio_m, float* scores, int64_t ld_scores,
+                     int32_t* n_visible, void* stream) {
+  if (T < 0) return CSA_ERR_INVALID_ARG;
+  if (T == 0) return CSA_OK;
+  if (!(q_idx_scale > 0.0f) || !(k_idx_scale > 0.0f) || !std::isfinite(q_idx_scale) || !std::isfinite(k_idx_scale))
+    return CSA_ERR_INVALID_ARG;
+  IndexParams p{};
+  p.q_idx = q_idx;
+  p.w = w;
+  p.k_idx = k_idx;
+  p.qk_scale = q_idx_scale * k_idx_scale;
+  return index_scores_common(p, page_table, n_comp, num_pages, page_size, max_pages, B, q_pos, q_seq, T, H_I, D_I,
+                             ratio_m, scores, ld_scores, n_visible, stream);
+}
+
+int csa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_idx_sc, const float* w, const uint8_t* k_idx,
+                           const uint8_t* k_idx_sc, const int32_t* page_table, const int32_t* n_comp,
+                           int32_t num_pages, int32_t page_size, int32_t max_pages, int32_t B, const int32_t* q_pos,
+                           const int32_t* q_seq, int32_t T, int32_t H_I, int32_t D_I, int32_t ratio_m,
+                           float* scores, int64_t ld_scores, int32_t* n_visible, void* stream) {
+  if (T < 0) return CSA_ERR_INVALID_ARG;
+  if (T == 0) return CSA_OK;
+  if (!q_idx_sc || !k_idx_sc) return CSA_ERR_INVALID_ARG;
+  IndexParams p{};
+  p.q_idx = q_idx;
+  p.w = w;
+  p.k_idx = k_idx;
+  p.q_sc = q_idx_sc;
+  p.k_sc = k_idx_sc;
+  p.fp4 = 1;
+  p.qk_scale = 1.0f;
+  return index_scores_common(p, page_table, n_comp, num_pages, page_size, max_pages, B, q_pos, q_seq, T, H_I, D_I,
+                             ratio_m, scores, ld_scores, n_visible, stream);
 }
 
 size_t csa_topk_workspace_size(int32_t T, int64_t ld_scores, int32_t k) {

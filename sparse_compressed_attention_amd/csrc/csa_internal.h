@@ -19,7 +19,10 @@ struct IndexParams {
   float* scores;
   int32_t* n_visible;
   int64_t ld;
-  float qk_scale;     // q_idx_scale * k_idx_scale
+  float qk_scale;     // q_idx_scale * k_idx_scale (1 for MXFP4)
+  const uint8_t* q_sc; // MXFP4: E8M0 scales [T][H_I][D_I / 32] and
+  const uint8_t* k_sc; //        [num_pages][page_size][D_I / 32]
+  int fp4;             // q_idx / k_idx are MXFP4 (E2M1 pairs) instead of E4M3
   int num_pages, page_size, max_pages, B;
   int T, H_I, D_I, ratio_m;
   int chunk, n_chunks;   // set by the launcher

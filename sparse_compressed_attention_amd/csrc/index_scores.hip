@@ -71,7 +71,14 @@ __device__ __forceinline__ float reduce4_scatter(float x0, float x1, float x2, f
 // kWaves * kGroups * 16 consecutive entries of one query row.  kQLds: the
 // workgroup reads the query operand from memory once and hands it to its
 // waves through LDS (else every wave loads its own copy).
-template <int kWaves, int kGroups, int kOcc, bool kQLds>
+//
+// kFp4: MXFP4 operands (the pages' FP4 indexer variant, "DSV4 Audit", B2):
+// q and k rows are E2M1 codes, two per byte (even element in the low
+// nibble), with one E8M0 scale per 32 dims; a lane's 32 dims are exactly one
+// scale block, so each lane hands its block's scale byte to the scaled MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4, FP4 x FP4).  A key row is D_I / 2
+// bytes plus D_I / 32 scale bytes: about half the bytes of the FP8 scan.
+template <int kWaves, int kGroups, int kOcc, bool kQLds, bool kFp4>
 __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexParams p) {
   static_assert(!kQLds || kWaves >= 4, "four waves fill the shared query operand");
   static_assert(kGroups <= 64, "one page-id lane per group");
@@ -79,6 +86,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   constexpr int kWaveEntries = 16 * kGroups;
   constexpr int kChunk = kWaves * kWaveEntries;
   __shared__ v8i qs[kQLds ? 4 * 64 : 1];
+  __shared__ int qss[kQLds && kFp4 ? 4 * 64 : 1];
   const int t = blockIdx.x / p.n_chunks;
   const int chunk = blockIdx.x - t * p.n_chunks;
   const int lane = threadIdx.x & 63;
@@ -92,22 +100,31 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   // is waited for.  Query operand: 4 tiles of 16 index heads; lane holds
   // head 16 ht + r, dims [32 g, 32 g + 32).  Weights of output rows
   // (heads 16 ht + 4 g + i), read as one 16-byte load per tile.
-  auto load_q = [&](int ht) -> v8i {
+  auto load_q = [&](int ht, int& sc) -> v8i {
     const int h = 16 * ht + r;
     v8i a = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    sc = 0;
     if (h < p.H_I && dim_ok) {
-      const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
-      const v4i lo = ld16(src), hi = ld16(src + 16);
-      a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const size_t row = (size_t)t * p.H_I + h;
+      if constexpr (kFp4) {
+        const v4i v = ld16(p.q_idx + row * (p.D_I / 2) + 16 * g);
+        a = (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        sc = p.q_sc[row * (p.D_I / 32) + g];
+      } else {
+        const uint8_t* src = p.q_idx + row * p.D_I + 32 * g;
+        const v4i lo = ld16(src), hi = ld16(src + 16);
+        a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     }
     return a;
   };
   v8i qa[4];
+  int qsc[4] = {0, 0, 0, 0};
   if (kQLds) {
-    if (wave < 4) qa[0] = load_q(wave);   // wave w < 4 fetches tile w
+    if (wave < 4) qa[0] = load_q(wave, qsc[0]);   // wave w < 4 fetches tile w
   } else {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) qa[ht] = load_q(ht);
+    for (int ht = 0; ht < 4; ++ht) qa[ht] = load_q(ht, qsc[ht]);
   }
   v4f wv[4];
 #pragma unroll
@@ -145,6 +162,7 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   // e_begin + 16 u + (0..15); lane (g, r) loads entry r's dims [32 g, 32 g + 32).
   int poff = e_begin % p.page_size;        // uniform: offset of group u in its page
   v8i kb[kGroups];
+  int ksc[kGroups];
   uint32_t ok_mask = 0;                    // uniform: group has a valid page
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) {
@@ -153,21 +171,36 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
     const bool ok = e0 < e_end && page >= 0 && page < p.num_pages;
     ok_mask |= (ok ? 1u : 0u) << u;
     v8i x = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    int xs = 0;
     if (ok && dim_ok && e0 + r < e_end) {
-      const uint8_t* src = p.k_idx + ((size_t)page * p.page_size + poff + r) * p.D_I + 32 * g;
-      const v4i lo = ld16(src), hi = ld16(src + 16);
-      x = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const size_t row = (size_t)page * p.page_size + poff + r;
+      if constexpr (kFp4) {
+        const v4i v = ld16(p.k_idx + row * (p.D_I / 2) + 16 * g);
+        x = (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        xs = p.k_sc[row * (p.D_I / 32) + g];
+      } else {
+        const uint8_t* src = p.k_idx + row * p.D_I + 32 * g;
+        const v4i lo = ld16(src), hi = ld16(src + 16);
+        x = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     }
     kb[u] = x;
+    ksc[u] = xs;
     poff += 16;
     if (poff >= p.page_size) poff -= p.page_size;
   }
   if (kQLds) {
     // the query tile arrived with the page ids, ahead of the keys
-    if (wave < 4) qs[wave * 64 + lane] = qa[0];
+    if (wave < 4) {
+      qs[wave * 64 + lane] = qa[0];
+      if constexpr (kFp4) qss[wave * 64 + lane] = qsc[0];
+    }
     lds_barrier();
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) qa[ht] = qs[ht * 64 + lane];
+    for (int ht = 0; ht < 4; ++ht) {
+      qa[ht] = qs[ht * 64 + lane];
+      if constexpr (kFp4) qsc[ht] = qss[ht * 64 + lane];
+    }
   }
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) wv[ht] *= p.qk_scale;
@@ -177,17 +210,23 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   // weighted ReLU of group u; every four groups one reduce-scatter over the
   // lane groups, after which lane (g, r) holds entry r of group 4 j + g
   float* out = p.scores + (size_t)t * p.ld;
-  auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
+  auto mfmas = [&](const v8i& k, int ks, v4f (&acc)[4]) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-      acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});   // rows of absent heads are zero
+    for (int ht = 0; ht < 4; ++ht) {
+      // rows of absent heads are zero
+      if constexpr (kFp4)
+        acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                                   qsc[ht], 0, ks);
+      else
+        acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});
+    }
   };
   v4f acc[2][4];
   float xg[4];
-  mfmas(kb[0], acc[0]);
+  mfmas(kb[0], ksc[0], acc[0]);
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) {
-    if (u + 1 < kGroups) mfmas(kb[u + 1], acc[(u + 1) & 1]);
+    if (u + 1 < kGroups) mfmas(kb[u + 1], ksc[u + 1], acc[(u + 1) & 1]);
     xg[u & 3] = wrelu16(acc[u & 1], wv);
     if ((u & 3) == 3) {
       const float tot = reduce4_scatter(xg[0], xg[1], xg[2], xg[3]);
@@ -363,15 +402,15 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   }
 }
 
-template <int kWaves, int kGroups, int kOcc, bool kQLds>
+template <int kWaves, int kGroups, int kOcc, bool kQLds, bool kFp4>
 hipError_t launch_decode(IndexParams p, int64_t span, hipStream_t stream) {
   constexpr int kChunk = kWaves * kGroups * 16;
   p.chunk = kChunk;
   p.n_chunks = (int)std::max<int64_t>(1, (span + kChunk - 1) / kChunk);
   const int64_t blocks = (int64_t)p.T * p.n_chunks;
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((index_scores_kernel<kWaves, kGroups, kOcc, kQLds>), dim3((unsigned)blocks), dim3(64 * kWaves), 0,
-                     stream, p);
+  hipLaunchKernelGGL((index_scores_kernel<kWaves, kGroups, kOcc, kQLds, kFp4>), dim3((unsigned)blocks),
+                     dim3(64 * kWaves), 0, stream, p);
   return hipPeekAtLastError();
 }
 
@@ -380,6 +419,9 @@ hipError_t launch_decode(IndexParams p, int64_t span, hipStream_t stream) {
 hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
   IndexParams p = p_in;
   const int64_t span = std::min<int64_t>(p.ld, (int64_t)p.max_pages * p.page_size);
+  // MXFP4 operands: the one-query kernel for every shape, with twice the
+  // groups per wave (a key row is half as long, so the same bytes in flight)
+  if (p.fp4) return launch_decode<4, 8, 4, true, true>(p, span, stream);
   if (p.B == 1 && p.T >= 2 * kMqQ) {
     // one sequence, many queries: key tiles shared through LDS
     p.chunk = kMqChunk;
@@ -392,7 +434,7 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
                        n_split);
     return hipPeekAtLastError();
   }
-  return launch_decode<4,4,4,true>(p, span, stream);
+  return launch_decode<4, 4, 4, true, false>(p, span, stream);
 }
 
 }  // namespace csa

@@ -31,9 +31,9 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(wl, inv_rope_theta=0.0):
+def run_gpu(wl, inv_rope_theta=0.0, mxfp4=False):
     d = to_device(wl, "cuda")
-    path = make_path(d, inv_rope_theta=inv_rope_theta)
+    path = make_path(d, inv_rope_theta=inv_rope_theta, mxfp4=mxfp4)
     out, lse = path.run()
     torch.cuda.synchronize()
     res = dict(o=out.float().cpu().numpy().astype(np.float64), lse=lse.cpu().numpy().astype(np.float64))
@@ -44,11 +44,12 @@ def run_gpu(wl, inv_rope_theta=0.0):
     return res
 
 
-def check_full(wl, queries=None, exact_topk_expected=None, inv_rope_theta=0.0):
+def check_full(wl, queries=None, exact_topk_expected=None, inv_rope_theta=0.0, mxfp4=False):
     """Run the whole path on the GPU and compare the listed queries (with the
-    inverse-RoPE epilogue when inv_rope_theta > 0)."""
+    inverse-RoPE epilogue when inv_rope_theta > 0; with the MXFP4 indexer
+    inputs when mxfp4)."""
     s = wl.spec
-    res = run_gpu(wl, inv_rope_theta)
+    res = run_gpu(wl, inv_rope_theta, mxfp4)
     qs = list(range(wl.T)) if queries is None else list(queries)
     worst = (0.0, 1.0)
     sc_err = 0.0
@@ -58,7 +59,7 @@ def check_full(wl, queries=None, exact_topk_expected=None, inv_rope_theta=0.0):
         nv = oracle.n_visible(int(wl.q_pos[t]), s.m, int(wl.n_comp[b]))
         if wl.q_idx is not None:
             assert int(res["n_vis"][t]) == nv
-            ref_scores = oracle.index_scores(wl, t)
+            ref_scores = oracle.index_scores_mxfp4(wl, t) if mxfp4 else oracle.index_scores(wl, t)
             sc_err = max(sc_err, P.check_scores(res["scores"][t][:nv], ref_scores) or 0.0)
             P.check_topk_exact_on_gpu_scores(res["topk"][t], res["scores"][t][:nv], s.k)
             exact += P.check_topk_vs_oracle(res["topk"][t], ref_scores, s.k)
@@ -70,7 +71,8 @@ def check_full(wl, queries=None, exact_topk_expected=None, inv_rope_theta=0.0):
             o_ref = oracle.inverse_rope(o_ref, int(wl.q_pos[t]), s.D_nope, inv_rope_theta)
         err, cos = P.check_attention(res["o"][t], res["lse"][t], o_ref, l_ref)
         worst = (max(worst[0], err), min(worst[1], cos))
-    say(f"  {s.name}{' (inverse RoPE)' if inv_rope_theta else ''}: {len(qs)} queries, max|err| {worst[0]:.3e}, min cos {worst[1]:.6f}, "
+    tag = (" (inverse RoPE)" if inv_rope_theta else "") + (" (MXFP4 indexer)" if mxfp4 else "")
+    say(f"  {s.name}{tag}: {len(qs)} queries, max|err| {worst[0]:.3e}, min cos {worst[1]:.6f}, "
         f"score err {sc_err:.2e} of row max, exact top-k sets {exact}/{len(qs)}")
     return res
 
@@ -187,6 +189,37 @@ def test_inverse_rope_full_size(name, queries, theta):
     # c3: positions near 2^19, where the angle needs its FP64 reduction
     say(f"case inverse RoPE full size {name}")
     check_full(ci.make_config(name), queries=queries, inv_rope_theta=theta)
+
+
+# --------------------------------------------------------------- MXFP4 indexer
+@pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "prefill_small", "tiny_dims_wide"])
+def test_mxfp4_indexer(case):
+    say(f"case MXFP4 indexer {case}")
+    qs = None
+    if case == "c0":
+        wl = ci.make_config("c0", mxfp4=True)
+    elif case == "small_ragged":
+        wl = ci.generate(ci.small_spec(shuffle_pages=True, mxfp4=True), seed=141)
+    elif case == "many_sequences":
+        spec = ci.small_spec(ctx_lens=[4096, 2052, 2500, 3332, 1028, 4100, 2600], shuffle_pages=True, k=384,
+                             mxfp4=True)
+        wl = ci.generate(spec, seed=142)
+    elif case == "prefill_small":
+        spec = ci.Spec(name="prefill_small", kind="prefill", ctx_lens=[6000], T_prefill=70, mxfp4=True)
+        wl, qs = ci.generate(spec, seed=143), [0, 1, 17, 33, 50, 69]
+    else:
+        rng = np.random.default_rng(144)
+        lens = [int(x) * 4 for x in rng.integers(40, 160, size=300)]
+        spec = ci.Spec(name="tiny_decode_300", kind="decode", ctx_lens=lens, H=8, D_nope=48, D_rope=16, H_I=4,
+                       D_I=32, k=16, W=32, page_size=16, shuffle_pages=True, mxfp4=True)
+        wl, qs = ci.generate(spec, seed=144), [0, 1, 150, 299]
+    check_full(wl, queries=qs, mxfp4=True)
+
+
+@pytest.mark.parametrize("name,queries", [("c2", [0, 21, 63]), ("c3_csa", [0, 2])])
+def test_mxfp4_indexer_full_size(name, queries):
+    say(f"case MXFP4 indexer full size {name}")
+    check_full(ci.make_config(name, mxfp4=True), queries=queries, mxfp4=True)
 
 
 def test_ring_permutation_invariance_gpu():
