@@ -254,6 +254,11 @@ constexpr int kMqGpw = kMqGroups / kMqQ;    // groups loaded per wave per chunk
 static_assert(kMqGroups % kMqQ == 0, "groups split evenly over the waves");
 static_assert(kMqGroups % 4 == 0, "groups are reduced four at a time");
 
+//
+// kFp4 (MXFP4 operands, as in the one-query kernel): a lane's LDS slot of a
+// group holds its 16 code bytes in dwords 0-3 and its block's scale byte in
+// dword 4; the scaled MFMA reads only dwords 0-3 of an FP4 operand.
+template <bool kFp4>
 __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexParams p, int n_split) {
   __shared__ __attribute__((aligned(16))) v8i ks[2][kMqGroups * 64];
   __shared__ uint32_t okw[2][kMqQ];
@@ -273,15 +278,24 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   // ---- this wave's query operand and weights (layout as in the
   // one-query kernel)
   v8i qa[4];
+  int qsc[4];
   v4f wv[4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const int h = 16 * ht + r;
     qa[ht] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    qsc[ht] = 0;
     if (q_ok && h < p.H_I && dim_ok) {
-      const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
-      const v4i lo = ld16(src), hi = ld16(src + 16);
-      qa[ht] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const size_t row = (size_t)t * p.H_I + h;
+      if constexpr (kFp4) {
+        const v4i v = ld16(p.q_idx + row * (p.D_I / 2) + 16 * g);
+        qa[ht] = (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        qsc[ht] = p.q_sc[row * (p.D_I / 32) + g];
+      } else {
+        const uint8_t* src = p.q_idx + row * p.D_I + 32 * g;
+        const v4i lo = ld16(src), hi = ld16(src + 16);
+        qa[ht] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     }
     const int h0 = 16 * ht + 4 * g;
 #pragma unroll
@@ -331,9 +345,15 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
       okbits |= (ok ? 1u : 0u) << u;
       kl[j] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
       if (ok && dim_ok && eg + r < nv_max) {
-        const uint8_t* src = p.k_idx + ((size_t)page * p.page_size + eg % p.page_size + r) * p.D_I + 32 * g;
-        const v4i lo = ld16(src), hi = ld16(src + 16);
-        kl[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const size_t row = (size_t)page * p.page_size + eg % p.page_size + r;
+        if constexpr (kFp4) {
+          const v4i v = ld16(p.k_idx + row * (p.D_I / 2) + 16 * g);
+          kl[j] = (v8i){v[0], v[1], v[2], v[3], (int)p.k_sc[row * (p.D_I / 32) + g], 0, 0, 0};
+        } else {
+          const uint8_t* src = p.k_idx + row * p.D_I + 32 * g;
+          const v4i lo = ld16(src), hi = ld16(src + 16);
+          kl[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
     }
   };
@@ -358,8 +378,14 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   float* out = p.scores + (size_t)t * p.ld;
   auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-      acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});   // rows of absent heads are zero
+    for (int ht = 0; ht < 4; ++ht) {
+      // rows of absent heads are zero
+      if constexpr (kFp4)
+        acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                                   qsc[ht], 0, k[4]);
+      else
+        acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});
+    }
   };
 
   for (int c = c_begin; c < n_ch; ++c) {
@@ -419,9 +445,6 @@ hipError_t launch_decode(IndexParams p, int64_t span, hipStream_t stream) {
 hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
   IndexParams p = p_in;
   const int64_t span = std::min<int64_t>(p.ld, (int64_t)p.max_pages * p.page_size);
-  // MXFP4 operands: the one-query kernel for every shape, with twice the
-  // groups per wave (a key row is half as long, so the same bytes in flight)
-  if (p.fp4) return launch_decode<4, 8, 4, true, true>(p, span, stream);
   if (p.B == 1 && p.T >= 2 * kMqQ) {
     // one sequence, many queries: key tiles shared through LDS
     p.chunk = kMqChunk;
@@ -430,10 +453,17 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
     const int64_t span_ch = std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
     // about two workgroups per CU (256 CUs), parts of at least 4 chunks
     const int n_split = (int)std::max<int64_t>(1, std::min<int64_t>((512 + n_qb - 1) / n_qb, span_ch / 4));
-    hipLaunchKernelGGL(index_scores_mq_kernel, dim3((unsigned)(n_qb * n_split)), dim3(64 * kMqQ), 0, stream, p,
-                       n_split);
+    if (p.fp4)
+      hipLaunchKernelGGL(index_scores_mq_kernel<true>, dim3((unsigned)(n_qb * n_split)), dim3(64 * kMqQ), 0, stream,
+                         p, n_split);
+    else
+      hipLaunchKernelGGL(index_scores_mq_kernel<false>, dim3((unsigned)(n_qb * n_split)), dim3(64 * kMqQ), 0, stream,
+                         p, n_split);
     return hipPeekAtLastError();
   }
+  // MXFP4 operands: twice the groups per wave (a key row is half as long, so
+  // the same bytes in flight)
+  if (p.fp4) return launch_decode<4, 8, 4, true, true>(p, span, stream);
   return launch_decode<4, 4, 4, true, false>(p, span, stream);
 }
 

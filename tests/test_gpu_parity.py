@@ -216,7 +216,7 @@ def test_mxfp4_indexer(case):
     check_full(wl, queries=qs, mxfp4=True)
 
 
-@pytest.mark.parametrize("name,queries", [("c2", [0, 21, 63]), ("c3_csa", [0, 2])])
+@pytest.mark.parametrize("name,queries", [("c2", [0, 21, 63]), ("c3_csa", [0, 2]), ("c4", [0, 1024, 2047])])
 def test_mxfp4_indexer_full_size(name, queries):
     say(f"case MXFP4 indexer full size {name}")
     check_full(ci.make_config(name, mxfp4=True), queries=queries, mxfp4=True)
