@@ -1,4 +1,5 @@
-// Step 1 of the CSA path: lightning-indexer scores on FP8 MFMA.
+// Step 1 of the CSA path: lightning-indexer scores on FP8 MFMA (and, as a
+// variant, on MXFP4 operands with the scaled FP4 MFMA).
 //
 // "DSV4 Audit -- Decode Repetition + Precision / Tensor-Core Plan", B2: the
 // indexer logits are the einsum 'tnd,cd->tnc' of per-token index queries

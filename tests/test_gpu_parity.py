@@ -166,11 +166,18 @@ def test_single_tile_key_range():
 # The epilogue runs in three places: the attention kernel's last dim part
 # when a workgroup writes the final output (four parts: decode batches that
 # fill the GPU; two parts: prefill), and the split merge (few queries).
-@pytest.mark.parametrize("case", ["c0_merge", "small_merge", "prefill_two_parts", "tiny_prefill_two_parts"])
+@pytest.mark.parametrize("case", ["c0_merge", "small_merge", "prefill_two_parts", "tiny_prefill_two_parts",
+                                  "partial_head_tiles"])
 def test_inverse_rope_epilogue(case):
     say(f"case inverse RoPE {case}")
     if case == "c0_merge":
         wl, qs = ci.make_config("c0"), None
+    elif case == "partial_head_tiles":
+        # 40 heads in 64-head workgroups (260 queries need no key split): one
+        # head tile has 8 valid heads, so some lanes skip the store while the
+        # pair swaps still run in every lane, and one tile has none
+        spec = ci.Spec(name="prefill_h40", kind="prefill", ctx_lens=[6000], T_prefill=260, H=40)
+        wl, qs = ci.generate(spec, seed=124), [0, 130, 259]
     elif case == "small_merge":
         wl, qs = ci.generate(ci.small_spec(shuffle_pages=True), seed=121), None
     elif case == "prefill_two_parts":
