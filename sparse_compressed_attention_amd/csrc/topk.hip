@@ -41,14 +41,16 @@ constexpr int kBins = 1 << kDigitBits;
 template <int BLOCK>
 struct TopkShared {
   static constexpr int kWaves = BLOCK / 64;
-  int hist[kBins];
+  // two histograms: a pass clears the next pass's while it finds its digit
+  int hist[2][kBins];
   int wsum[kWaves];
   int sel[4];
   uint32_t red[2][kWaves];
 };
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
-// the sum of all.  Contains barriers: every thread must call it.
+// the sum of all.  Contains a barrier: every thread must call it, and two
+// calls must be separated by another barrier (the per-wave sums are reused).
 template <int BLOCK>
 __device__ int block_exclusive_scan(int v, TopkShared<BLOCK>& sh, int* total) {
   const int lane = threadIdx.x & 63;
@@ -68,7 +70,6 @@ __device__ int block_exclusive_scan(int v, TopkShared<BLOCK>& sh, int* total) {
     before += (w < wave) ? s : 0;
     tot += s;
   }
-  __syncthreads();
   *total = tot;
   return before + x - v;
 }
@@ -88,6 +89,7 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
   constexpr int kBpt = kBins / BLOCK;   // histogram bins per thread in the scan
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kBins; i += BLOCK) sh.hist[0][i] = 0;
   // smallest / largest valid key of the workgroup
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -126,15 +128,14 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
   s.pmask = top == 31 ? 0u : ~((2u << top) - 1u);
   s.prefix = kmax & s.pmask;
   int rem = K;
+  int hb = 0;                            // this pass's histogram (cleared)
   while (true) {
     const int nb = top + 1 < kDigitBits ? top + 1 : kDigitBits;
     const int lo = top - nb + 1;
     const uint32_t dmask = (1u << nb) - 1u;
-    for (int i = threadIdx.x; i < kBins; i += BLOCK) sh.hist[i] = 0;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
-      if (((valid >> j) & 1u) && (key[j] & s.pmask) == s.prefix) atomicAdd(&sh.hist[(key[j] >> lo) & dmask], 1);
+      if (((valid >> j) & 1u) && (key[j] & s.pmask) == s.prefix) atomicAdd(&sh.hist[hb][(key[j] >> lo) & dmask], 1);
     }
     __syncthreads();
     // thread t owns bins 2047 - kBpt t - i, i < kBpt (descending digit order)
@@ -142,7 +143,7 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
     int tsum = 0;
 #pragma unroll
     for (int i = 0; i < kBpt; ++i) {
-      c[i] = sh.hist[kBins - 1 - (kBpt * threadIdx.x + i)];
+      c[i] = sh.hist[hb][kBins - 1 - (kBpt * threadIdx.x + i)];
       tsum += c[i];
     }
     int tot;
@@ -159,11 +160,16 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
         acc += c[i];
       }
     }
+    // the next pass's histogram: its last reads were before this pass's
+    // scan barrier
+    for (int i = threadIdx.x; i < kBins; i += BLOCK) sh.hist[hb ^ 1][i] = 0;
     __syncthreads();
+    // sel is written again only after the next pass's histogram barrier,
+    // which every thread reaches after reading it here
     const uint32_t d = (uint32_t)sh.sel[0];
     const int above = sh.sel[1];
     const int in_bin = sh.sel[2];
-    __syncthreads();
+    hb ^= 1;
     s.prefix |= d << lo;
     s.pmask |= dmask << lo;
     rem -= above;
@@ -188,10 +194,16 @@ __device__ void emit_selected(const uint32_t (&key)[SEG], uint32_t valid, const 
       eq += m == s.prefix;
     }
   }
+  static_assert(kTopkMaxChunk < 65536 && kTopkMaxCand < 65536, "packed 16-bit counts");
+  // one scan of both counts, packed as (gt << 16) | eq: over a workgroup each
+  // sum is at most 16384, so the low half never carries into the high half;
+  // the keys equal to the prefix are taken in position order, so the ones
+  // taken before this thread are min(eq_before, need_eq)
   int tot;
-  const int eq_before = block_exclusive_scan(eq, sh, &tot);
+  const int packed = block_exclusive_scan((gt << 16) | eq, sh, &tot);
+  const int gt_before = packed >> 16, eq_before = packed & 0xffff;
   const int take_eq = max(0, min(eq, s.need_eq - eq_before));
-  int off = block_exclusive_scan(gt + take_eq, sh, &tot);
+  int off = gt_before + min(eq_before, s.need_eq);
   int eq_seen = 0;
 #pragma unroll
   for (int j = 0; j < SEG; ++j) {
