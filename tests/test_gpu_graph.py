@@ -44,11 +44,16 @@ def same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("case", ["c0", "small_decode", "hca_small", "prefill_small"])
+@pytest.mark.parametrize("case", ["c0", "small_decode", "hca_small", "prefill_small", "mxfp4_inv_rope"])
 def test_graph_replay_matches_eager(case):
     say(f"case graph replay {case}")
+    opts = {}
     if case == "c0":
         wl = ci.make_config("c0")
+    elif case == "mxfp4_inv_rope":
+        # the variant entry points are captured as well
+        wl = ci.generate(ci.small_spec(shuffle_pages=True, mxfp4=True), seed=136)
+        opts = dict(mxfp4=True, inv_rope_theta=10000.0)
     elif case == "small_decode":
         wl = ci.generate(ci.small_spec(shuffle_pages=True), seed=131)
     elif case == "hca_small":
@@ -56,7 +61,7 @@ def test_graph_replay_matches_eager(case):
     else:
         wl = ci.generate(ci.Spec(name="prefill_small", kind="prefill", ctx_lens=[6000], T_prefill=70), seed=133)
     d = to_device(wl, "cuda")
-    path = make_path(d)
+    path = make_path(d, **opts)
     path.run()
     eager = snapshot(path)
     g = csa.StepGraph(path)

@@ -199,12 +199,23 @@ def test_inverse_rope_full_size(name, queries, theta):
 
 
 # --------------------------------------------------------------- MXFP4 indexer
-@pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "prefill_small", "tiny_dims_wide"])
+@pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "prefill_small", "tiny_dims_wide",
+                                  "heads40_dims64", "heads24_dims96_prefill"])
 def test_mxfp4_indexer(case):
     say(f"case MXFP4 indexer {case}")
     qs = None
     if case == "c0":
         wl = ci.make_config("c0", mxfp4=True)
+    elif case == "heads40_dims64":
+        # partial index-head tiles and two scale blocks per row
+        spec = ci.small_spec(name="fp4_h40_d64", ctx_lens=[2600, 1400], H_I=40, D_I=64, shuffle_pages=True,
+                             mxfp4=True)
+        wl = ci.generate(spec, seed=145)
+    elif case == "heads24_dims96_prefill":
+        # the multi-query kernel with three scale blocks per row
+        spec = ci.Spec(name="fp4_prefill_h24_d96", kind="prefill", ctx_lens=[5000], T_prefill=40, H_I=24, D_I=96,
+                       mxfp4=True)
+        wl, qs = ci.generate(spec, seed=146), [0, 13, 39]
     elif case == "small_ragged":
         wl = ci.generate(ci.small_spec(shuffle_pages=True, mxfp4=True), seed=141)
     elif case == "many_sequences":
