@@ -323,7 +323,7 @@ def main():
     dom_name = stages[dom]
     roof = roofline_entry(dom_name, acc[dom_name], per_stage[dom])
     roof["kernel"] = dom_name
-    roof["traffic"] = measured_traffic(name, dom_name)
+    roof["traffic"] = measured_traffic(name + ("_mxfp4" if fp4 else ""), dom_name)
 
     out = dict(
         metric=PREFILL_METRIC if wl.spec.kind == "prefill" else BASE_METRIC,
