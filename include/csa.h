@@ -32,16 +32,19 @@
  * --------------------------------
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except
  *    the two struct pointers (csa_latent_cache*, csa_swa_ring*), which point
- *    to HOST structs read during the call.  No call keeps a pointer after it
- *    returns, allocates device memory, or synchronises the device.  Work is
- *    enqueued on `stream` (a hipStream_t passed as void*; NULL = default
- *    stream) and runs asynchronously.
+ *    to HOST structs read during the call.  No step call (csa_index_scores*,
+ *    csa_topk, csa_*_attn) keeps a pointer after it returns, allocates
+ *    device memory, or synchronises the device; the csa_graph_* calls
+ *    create and free graph objects and are meant for set-up, not for the
+ *    step itself.  Work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL = default stream) and runs asynchronously.
  *  - Return value: CSA_OK (0) or a negative error code.  Argument errors are
  *    detected on the host before any launch (nothing is enqueued).  Launch
  *    errors are detected with hipPeekAtLastError() after the launch.
  *  - Data formats: E4M3 = OCP FP8 E4M3FN bytes; BF16 = bfloat16 bit
  *    patterns in uint16_t.  Each FP8 tensor carries one float "scale": the
- *    stored value times the scale is the real value.
+ *    stored value times the scale is the real value (MXFP4 tensors carry
+ *    block scales instead; see csa_index_scores_mxfp4).
  *  - Latent layout: D = D_nope + D_rope dims, nope dims first.  K = V =
  *    the whole latent, shared by all query heads.
  *  - Positions are absolute, 0-based; a query's context includes its own
