@@ -117,7 +117,8 @@ typedef struct csa_swa_ring {
 } csa_swa_ring;
 
 /* ---- Step 1: indexer scores ([Audit] B2) ------------------------------
- * For each query row t (sequence q_seq[t], position q_pos[t]) and each
+ * For each query row t (sequence q_seq[t], or t when q_seq is NULL as in a
+ * decode batch; position q_pos[t]) and each
  * visible entry c < n_vis(t):
  *   scores[t*ld_scores + c] =
  *       sum_h w[t][h] * max(0, (q_idx_scale*q_idx[t][h][:]) .

@@ -198,7 +198,8 @@ def csa_index_scores(q_idx, q_idx_scale, w, k_idx, k_idx_scale, page_table, n_co
     _need(page_table, "page_table", _I32, 2)
     _need(n_comp, "n_comp", _I32, 1)
     _need(q_pos, "q_pos", _I32, 1)
-    _need(q_seq, "q_seq", _I32, 1)
+    if q_seq is not None:                  # None: query t belongs to sequence t
+        _need(q_seq, "q_seq", _I32, 1)
     _need(scores, "scores", _F32, 2, contiguous=False)
     _need(n_visible, "n_visible", _I32, 1)
     if scores.stride(1) != 1:
@@ -226,7 +227,8 @@ def csa_index_scores_mxfp4(q_idx, q_idx_sc, w, k_idx, k_idx_sc, page_table, n_co
     _need(page_table, "page_table", _I32, 2)
     _need(n_comp, "n_comp", _I32, 1)
     _need(q_pos, "q_pos", _I32, 1)
-    _need(q_seq, "q_seq", _I32, 1)
+    if q_seq is not None:                  # None: query t belongs to sequence t
+        _need(q_seq, "q_seq", _I32, 1)
     _need(scores, "scores", _F32, 2, contiguous=False)
     _need(n_visible, "n_visible", _I32, 1)
     if scores.stride(1) != 1:
@@ -378,7 +380,7 @@ class DecodePath(_Path):
         self.q_idx, self.q_idx_scale, self.w, self.k_idx, self.k_idx_scale = q_idx, q_idx_scale, w, k_idx, k_idx_scale
         _need(q, "q", _B16, 3)
         B, H, D = q.shape
-        self.q_seq = torch.arange(B, dtype=torch.int32, device=dev)
+        self.q_seq = None                  # the indexer's default: query b belongs to sequence b
         max_entries = cache.page_table.shape[1] * cache.nope.shape[1]
         self.ld = max(16, (max_entries + 15) // 16 * 16)
         self.out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)

@@ -130,7 +130,7 @@ static int index_scores_common(IndexParams& p, const int32_t* page_table, const 
                                int32_t page_size, int32_t max_pages, int32_t B, const int32_t* q_pos,
                                const int32_t* q_seq, int32_t T, int32_t H_I, int32_t D_I, int32_t ratio_m,
                                float* scores, int64_t ld_scores, int32_t* n_visible, void* stream) {
-  if (!p.q_idx || !p.w || !p.k_idx || !page_table || !n_comp || !q_pos || !q_seq || !scores || !n_visible)
+  if (!p.q_idx || !p.w || !p.k_idx || !page_table || !n_comp || !q_pos || !scores || !n_visible)
     return CSA_ERR_INVALID_ARG;
   if (!aligned16(p.q_idx) || !aligned16(p.k_idx)) return CSA_ERR_INVALID_ARG;
   if (B < 1 || num_pages < 1 || page_size < 16 || page_size % 16 || max_pages < 1 || ratio_m < 1 || ld_scores < 1)

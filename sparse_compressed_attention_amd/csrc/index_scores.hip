@@ -138,7 +138,9 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
       for (int i = 0; i < 4; ++i) wv[ht][i] = h0 + i < p.H_I ? p.w[(size_t)t * p.H_I + h0 + i] : 0.0f;
     }
   }
-  const int seq = p.q_seq[t];
+  // without q_seq, query t belongs to sequence t (a decode batch), and the
+  // page ids need no load before them
+  const int seq = p.q_seq ? p.q_seq[t] : t;
   const int pos = p.q_pos[t];
   const int e_begin = chunk * kChunk + wave * kWaveEntries;
   const bool seq_ok = seq >= 0 && seq < p.B;
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
     int nv = 0;
     if (tw < p.T) {
       const int pos = p.q_pos[tw];
-      if (p.q_seq[tw] == 0 && pos >= 0) nv = min(pos / p.ratio_m, nc);
+      if ((p.q_seq ? p.q_seq[tw] : tw) == 0 && pos >= 0) nv = min(pos / p.ratio_m, nc);
       nv = max(0, min(nv, (int)min<int64_t>(p.ld, 0x7fffffff)));
       if (split == 0 && w == wave && lane == 0) p.n_visible[tw] = nv;
     }

@@ -368,6 +368,41 @@ def test_topk_kernel_exact_on_synthetic_rows(k):
         assert np.array_equal(got[i], want), (k, n, kinds[i % len(kinds)])
 
 
+@pytest.mark.parametrize("fp4", [False, True])
+def test_indexer_explicit_query_sequences(fp4):
+    # rows that do not follow the decode default (row t = sequence t): two
+    # rows of one sequence, rows out of order, a position before the last
+    # stored block, and a row of a sequence beyond the cache (nothing visible)
+    say(f"case indexer with explicit q_seq (mxfp4={fp4})")
+    wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1508, 2400], shuffle_pages=True, mxfp4=True), seed=150)
+    rows = [2, 0, 1, 2, 0]
+    q_seq = np.array([2, 0, 1, 2, 7], dtype=np.int32)
+    q_pos = np.array([2399, 2999, 1400, 2000, 2999], dtype=np.int32)
+    wl2 = dataclasses.replace(wl, T=len(rows), q_idx=wl.q_idx[rows], w=wl.w[rows], q_idx4=wl.q_idx4[rows],
+                              q_idx4_sc=wl.q_idx4_sc[rows], q_seq=q_seq, q_pos=q_pos)
+    d = to_device(wl2, "cuda")
+    ld = 1024
+    scores = torch.full((wl2.T, ld), 7.0, dtype=torch.float32, device="cuda")
+    n_vis = torch.full((wl2.T,), -5, dtype=torch.int32, device="cuda")
+    qs, qp = torch.from_numpy(q_seq).cuda(), torch.from_numpy(q_pos).cuda()
+    if fp4:
+        csa.csa_index_scores_mxfp4(d.q_idx4, d.q_idx4_sc, d.w, d.k_idx4, d.k_idx4_sc, d.page_table, d.n_comp, qp, qs,
+                                   wl2.spec.m, scores, n_vis)
+    else:
+        csa.csa_index_scores(d.q_idx, d.q_idx_scale, d.w, d.k_idx, d.k_idx_scale, d.page_table, d.n_comp, qp, qs,
+                             wl2.spec.m, scores, n_vis)
+    torch.cuda.synchronize()
+    sc, nv = scores.cpu().numpy(), n_vis.cpu().numpy()
+    for t in range(wl2.T):
+        b = int(q_seq[t])
+        want_nv = oracle.n_visible(int(q_pos[t]), wl2.spec.m, int(wl2.n_comp[b])) if b < wl2.B else 0
+        assert int(nv[t]) == want_nv
+        if want_nv:
+            ref = oracle.index_scores_mxfp4(wl2, t) if fp4 else oracle.index_scores(wl2, t)
+            P.check_scores(sc[t][:want_nv], ref)
+    say(f"  n_visible {nv.tolist()}")
+
+
 @pytest.mark.parametrize("page_size", [16, 48, 64, 96])
 def test_indexer_page_sizes(page_size):
     say(f"case indexer page {page_size}")
