@@ -88,8 +88,11 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   constexpr int kChunk = kWaves * kWaveEntries;
   __shared__ v8i qs[kQLds ? 4 * 64 : 1];
   __shared__ int qss[kQLds && kFp4 ? 4 * 64 : 1];
-  const int t = blockIdx.x / p.n_chunks;
-  const int chunk = blockIdx.x - t * p.n_chunks;
+  // chunk-major grid: every row's first chunks are dispatched before any
+  // row's later ones, so the workgroups past a short row's visible range
+  // (which exit after one round trip) come last instead of between busy ones
+  const int chunk = blockIdx.x / p.T;
+  const int t = blockIdx.x - chunk * p.T;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
