@@ -39,6 +39,26 @@ def build_command(out_path: str) -> list[str]:
     ]
 
 
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "decode_step.cpp")
+C_DRIVER = os.path.join(ROOT, "tests", "c_abi", "decode_step")
+
+
+def build_c_driver(verbose: bool = False) -> str:
+    """The test driver that runs a decode step through the C ABI alone
+    (linked against libcsa.so next to this file)."""
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", INCLUDE, C_DRIVER_SRC, "-L", PKG_DIR, "-lcsa",
+           "-Wl,-rpath,$ORIGIN/../../sparse_compressed_attention_amd", "-o", C_DRIVER]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + msgs)
+    if verbose and msgs.strip():
+        print(msgs, file=sys.stderr)
+    return C_DRIVER
+
+
 def build(verbose: bool = False) -> str:
     fd, tmp = tempfile.mkstemp(prefix=".libcsa.", suffix=".so.tmp", dir=PKG_DIR)
     os.close(fd)
@@ -55,6 +75,7 @@ def build(verbose: bool = False) -> str:
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+    build_c_driver(verbose)
     return LIB_PATH
 
 
