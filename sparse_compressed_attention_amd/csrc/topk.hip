@@ -225,14 +225,17 @@ __global__ __launch_bounds__(BLOCK, 6) void topk_chunk_kernel(TopkParams p) {
   __shared__ TopkShared<BLOCK> sh;
   const int t = blockIdx.x / p.n_chunks;
   const int ch = blockIdx.x - t * p.n_chunks;
-  const int nv = (int)max<int64_t>(0, min<int64_t>(p.n_visible[t], p.ld));
+  const int nv_raw = p.n_visible[t];   // in flight together with the scores
   const int c0 = ch * p.chunk;
-  const int n = max(0, min(nv - c0, p.chunk));
   const int i0 = threadIdx.x * SEG;
-  const int cnt = max(0, min(SEG, n - i0));
+  // The scores are read without waiting for the visible count: a thread
+  // loads the part of its segment that lies inside the row's allocated
+  // columns [0, ld); columns past the visible count are masked below and
+  // never used.
+  const int avail = (int)max<int64_t>(0, min<int64_t>(SEG, min<int64_t>(p.ld - c0, p.chunk) - i0));
   const float* src = p.scores + (size_t)t * p.ld + c0 + i0;
   uint32_t key[SEG];
-  if (cnt == SEG && ((((uintptr_t)src) & 15) == 0)) {
+  if (avail == SEG && ((((uintptr_t)src) & 15) == 0)) {
     // whole segment: 16-byte loads
 #pragma unroll
     for (int j = 0; j < SEG; j += 4) {
@@ -242,8 +245,11 @@ __global__ __launch_bounds__(BLOCK, 6) void topk_chunk_kernel(TopkParams p) {
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < SEG; ++j) key[j] = j < cnt ? float_order_key(src[j]) : 0u;
+    for (int j = 0; j < SEG; ++j) key[j] = j < avail ? float_order_key(src[j]) : 0u;
   }
+  const int nv = (int)max<int64_t>(0, min<int64_t>(nv_raw, p.ld));
+  const int n = max(0, min(nv - c0, p.chunk));
+  const int cnt = max(0, min(SEG, n - i0));
   const uint32_t valid = cnt >= 32 ? 0xffffffffu : ((1u << cnt) - 1u);
   const int K = min(p.k, n);
   if (p.n_chunks == 1) {
