@@ -150,3 +150,19 @@ def test_graph_calls_reject_null_handles_without_gpu_work(lib):
     assert lib.csa_graph_capture_end(None, ctypes.byref(h)) == -1
     assert lib.csa_graph_launch(None, None) == -1
     lib.csa_graph_destroy(None)                          # no-op
+
+
+def test_attention_without_enough_workspace_is_rejected_before_launch(lib):
+    # HCA over up to 6400 entries needs its key range split over workgroups
+    # (at most 2048 slots each), so it needs the partial-result workspace
+    fake = ctypes.c_void_p(1 << 20)
+    cache = csa._LatentCacheC(1 << 20, 1 << 20, 1.0, 1 << 20, 1 << 20, 2, 8, 64, 100, 448, 64, 128)
+    ring = csa._SwaRingC(1 << 20, 1 << 20, 1.0, 1 << 20, 128)
+    need = lib.csa_attn_workspace_size(2, 128, 448, 64, 100 * 64 + 128)
+    assert need > 0
+    rc = lib.csa_decode_attn(fake, 512 * 128, ctypes.byref(cache), None, 0, ctypes.byref(ring), fake, fake,
+                             1.0, 0.0, 2, 128, fake, None, None, 0, None)
+    assert rc == -4      # no workspace
+    rc = lib.csa_decode_attn(fake, 512 * 128, ctypes.byref(cache), None, 0, ctypes.byref(ring), fake, fake,
+                             1.0, 0.0, 2, 128, fake, None, fake, 1024, None)
+    assert rc == -4      # far too small
