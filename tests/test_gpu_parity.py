@@ -167,11 +167,14 @@ def test_single_tile_key_range():
 # when a workgroup writes the final output (four parts: decode batches that
 # fill the GPU; two parts: prefill), and the split merge (few queries).
 @pytest.mark.parametrize("case", ["c0_merge", "small_merge", "prefill_two_parts", "tiny_prefill_two_parts",
-                                  "partial_head_tiles"])
+                                  "partial_head_tiles", "hca"])
 def test_inverse_rope_epilogue(case):
     say(f"case inverse RoPE {case}")
     if case == "c0_merge":
         wl, qs = ci.make_config("c0"), None
+    elif case == "hca":
+        spec = ci.small_spec(name="hca_small", ctx_lens=[20000, 9000, 41000], m=128, with_indexer=False)
+        wl, qs = ci.generate(spec, seed=125), None
     elif case == "partial_head_tiles":
         # 40 heads in 64-head workgroups (260 queries need no key split): one
         # head tile has 8 valid heads, so some lanes skip the store while the
@@ -232,6 +235,13 @@ def test_mxfp4_indexer(case):
                        D_I=32, k=16, W=32, page_size=16, shuffle_pages=True, mxfp4=True)
         wl, qs = ci.generate(spec, seed=144), [0, 1, 150, 299]
     check_full(wl, queries=qs, mxfp4=True)
+
+
+@pytest.mark.parametrize("page_size", [16, 96])
+def test_mxfp4_indexer_page_sizes(page_size):
+    say(f"case MXFP4 indexer page {page_size}")
+    spec = ci.small_spec(ctx_lens=[4000, 1508, 2900], shuffle_pages=True, page_size=page_size, mxfp4=True)
+    check_full(ci.generate(spec, seed=210 + page_size), mxfp4=True)
 
 
 @pytest.mark.parametrize("name,queries", [("c2", [0, 21, 63]), ("c3_csa", [0, 2]), ("c4", [0, 1024, 2047])])
