@@ -146,6 +146,23 @@ def test_decode_fewer_stored_entries_than_position_allows():
     check_full(dataclasses.replace(wl, n_comp=n_comp))
 
 
+def test_long_page_table_row_read_from_global_memory():
+    # more pages per sequence than the attention workgroup stages in LDS
+    # (tiny dims: 256 threads x 4 = 1024 page ids): 1100+ pages of 16 entries
+    say("case long page-table rows (global page-id path)")
+    spec = ci.Spec(name="tiny_long_pt", kind="decode", ctx_lens=[70400, 4000], H=8, D_nope=48, D_rope=16, H_I=4,
+                   D_I=32, k=16, W=32, page_size=16, shuffle_pages=True)
+    wl = ci.generate(spec, seed=117)
+    assert wl.max_pages > 1024
+    check_full(wl)
+    # and HCA mode over the same cache (every visible entry, many splits)
+    spec_h = ci.Spec(name="tiny_long_pt_hca", kind="decode", ctx_lens=[70400 * 8, 4000 * 8], H=8, D_nope=48,
+                     D_rope=16, k=16, W=32, page_size=16, m=32, with_indexer=False)
+    wl_h = ci.generate(spec_h, seed=118)
+    assert wl_h.max_pages > 1024
+    check_full(wl_h)
+
+
 def test_partial_head_tiles_production_dims():
     # 40 heads at the production latent: the second 32-head workgroup has one
     # head tile with 8 valid heads and one with none, and every tile runs on
