@@ -146,10 +146,9 @@ def test_decode_fewer_stored_entries_than_position_allows():
     check_full(dataclasses.replace(wl, n_comp=n_comp))
 
 
-def test_long_page_table_row_read_from_global_memory():
-    # more pages per sequence than the attention workgroup stages in LDS
-    # (tiny dims: 256 threads x 4 = 1024 page ids): 1100+ pages of 16 entries
-    say("case long page-table rows (global page-id path)")
+def test_long_page_table_rows():
+    # 1100 pages of 16 entries in one sequence's page-table row, shuffled
+    say("case long page-table rows")
     spec = ci.Spec(name="tiny_long_pt", kind="decode", ctx_lens=[70400, 4000], H=8, D_nope=48, D_rope=16, H_I=4,
                    D_I=32, k=16, W=32, page_size=16, shuffle_pages=True)
     wl = ci.generate(spec, seed=117)
