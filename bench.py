@@ -63,6 +63,8 @@ def parse():
                     help="replay each step from a captured graph (csa_graph_*) instead of issuing its calls")
     ap.add_argument("--mxfp4", action="store_true",
                     help="indexer on MXFP4 inputs (csa_index_scores_mxfp4) instead of E4M3")
+    ap.add_argument("--fused-topk", action="store_true",
+                    help="steps 1+2 as one call (csa_index_topk, decode only)")
     ap.add_argument("--inv-rope-theta", type=float, default=0.0,
                     help="base of the inverse-RoPE epilogue on the output's rope dims (0 = off)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -117,6 +119,9 @@ def accounting(wl, mxfp4=False):
             bytes=key_bytes + T * s.H_I * (idx_row + 4) + int(nv.sum()) * 4 + T * 4,
             flops=2.0 * s.H_I * s.D_I * float(nv.sum()))
         acc["topk"] = dict(bytes=int(nv.sum()) * 4 + T * s.k * 4 + T * 4, flops=0.0)
+        # fused steps 1+2: the scores stay on chip
+        acc["index_topk"] = dict(bytes=key_bytes + T * s.H_I * (idx_row + 4) + T * s.k * 4 + T * 4,
+                                 flops=acc["index_scores"]["flops"])
     keys = n_sel + n_win
     if s.kind == "decode":
         lat_bytes = int(keys.sum()) * row
@@ -143,9 +148,9 @@ def roofline_entry(name, a, ms):
 
 def kernel_source_sha(name):
     src = {"index_scores": "index_scores.hip", "topk": "topk.hip", "decode_attn": "attn.hip",
-           "prefill_attn": "attn.hip"}[name]
+           "prefill_attn": "attn.hip", "index_topk": "index_scores.hip"}[name]
     h = hashlib.sha256()
-    for f in (src, "csa_device.h", "csa_internal.h"):
+    for f in (src, "csa_device.h", "csa_internal.h", "topk_select.h"):
         with open(os.path.join(ROOT, "sparse_compressed_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -243,8 +248,8 @@ def main():
     copies = args.copies or int(min(256, max(2, math.ceil((1 << 30) / max(footprint, 1)))))
     theta = args.inv_rope_theta
     fp4 = args.mxfp4
-    paths = [make_path(d0, inv_rope_theta=theta, mxfp4=fp4)] + [
-        make_path(to_device(wl, dev), inv_rope_theta=theta, mxfp4=fp4) for _ in range(copies - 1)]
+    opts = dict(inv_rope_theta=theta, mxfp4=fp4, fused_topk=args.fused_topk)
+    paths = [make_path(d0, **opts)] + [make_path(to_device(wl, dev), **opts) for _ in range(copies - 1)]
     del d0
     stages = paths[0].stage_names
     stream = torch.cuda.current_stream()
@@ -334,6 +339,7 @@ def main():
         config=dict(workload=f"{name}: {WORKLOADS[name]}", queries_per_step=n_items, input_copies=copies,
                     gpu_ms_per_step=round(gpu_step, 5), launch="graph replay" if graphs else "eager calls",
                     inv_rope_theta=theta or None, indexer="MXFP4" if fp4 else "E4M3",
+                    fused_topk=bool(getattr(paths[0], "fused_topk", False)),
                     synced_step_latency=latency),
         roofline=roof,
         kernels=kernels,

@@ -5,6 +5,7 @@
  * The path has four steps, exposed as four calls (plus workspace queries):
  *   csa_index_scores  lightning-indexer scores            (step 1)
  *                     (csa_index_scores_mxfp4: FP4 operands)
+ *   csa_index_topk    steps 1+2 fused, scores kept on chip
  *   csa_topk          causal top-k over those scores      (step 2)
  *   csa_decode_attn   gather + sink attention, decode     (steps 3+4)
  *   csa_prefill_attn  gather + sink attention, prefill    (steps 3+4)
@@ -182,6 +183,31 @@ size_t csa_topk_workspace_size(int32_t T, int64_t ld_scores, int32_t k);
 int csa_topk(const float* scores, int64_t ld_scores, const int32_t* n_visible,
              int32_t T, int32_t k, int32_t* topk_idx,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Steps 1+2 fused ([Audit] B2: weighted-ReLU MQA logits and a top-k
+ * with a wave-local reduction and no global lock) --------------------------
+ * The result of csa_index_scores followed by csa_topk (same arguments, same
+ * selection rule, bit-identical indices), without writing the scores: one
+ * workgroup per (row, chunk of 2048, 4096 or 8192 entries) keeps its
+ * chunk's scores in LDS and selects the chunk's top-k there; rows longer
+ * than one chunk are finished by the top-k merge over the chunks'
+ * candidates.  Outputs: topk_idx [T][k] (ascending, -1 padding) and
+ * n_visible [T].  E4M3 operands only.
+ * Workspace: csa_index_topk_workspace_size(T, max_pages * page_size, k)
+ * bytes (0 when a row fits one chunk; NULL is then allowed).
+ * Supported: 1 <= k <= 2048 and (max_pages * page_size) / 8192 chunks of k
+ * candidates within the merge's 16384 (CSA_ERR_UNSUPPORTED otherwise).
+ * Errors: CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE,
+ * CSA_ERR_LAUNCH. */
+size_t csa_index_topk_workspace_size(int32_t T, int64_t max_entries, int32_t k);
+int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w,
+                   const uint8_t* k_idx, float k_idx_scale,
+                   const int32_t* page_table, const int32_t* n_comp,
+                   int32_t num_pages, int32_t page_size, int32_t max_pages, int32_t B,
+                   const int32_t* q_pos, const int32_t* q_seq, int32_t T,
+                   int32_t H_I, int32_t D_I, int32_t ratio_m, int32_t k,
+                   int32_t* topk_idx, int32_t* n_visible,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Steps 3+4: gather + shared-latent sink attention ----------------
  * For query t with key set J_t ([Audit] A3 "5. Gather KV"):

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "CsaError", "LatentCache", "SwaRing", "DecodePath", "PrefillPath", "library_path", "load_library",
-    "csa_index_scores", "csa_index_scores_mxfp4", "csa_topk", "csa_topk_workspace_size", "csa_attn_workspace_size",
+    "csa_index_scores", "csa_index_scores_mxfp4", "csa_index_topk", "csa_index_topk_workspace_size", "csa_topk", "csa_topk_workspace_size", "csa_attn_workspace_size",
     "csa_decode_attn", "csa_prefill_attn", "csa_status_string", "csa_version",
     "csa_graph_capture_begin", "csa_graph_capture_end", "csa_graph_launch", "csa_graph_destroy", "StepGraph",
 ]
@@ -68,6 +68,11 @@ def load_library():
     lib.csa_index_scores_mxfp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32,
                                            vp, i64, vp, vp]
     lib.csa_index_scores_mxfp4.restype = ctypes.c_int
+    lib.csa_index_topk_workspace_size.argtypes = [i32, i64, i32]
+    lib.csa_index_topk_workspace_size.restype = sz
+    lib.csa_index_topk.argtypes = [vp, f32, vp, vp, f32, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32, i32,
+                                   vp, vp, vp, sz, vp]
+    lib.csa_index_topk.restype = ctypes.c_int
     lib.csa_topk_workspace_size.argtypes = [i32, i64, i32]
     lib.csa_topk_workspace_size.restype = sz
     lib.csa_topk.argtypes = [vp, i64, vp, i32, i32, vp, vp, sz, vp]
@@ -246,6 +251,35 @@ def csa_index_scores_mxfp4(q_idx, q_idx_sc, w, k_idx, k_idx_sc, page_table, n_co
     _check("csa_index_scores_mxfp4", rc)
 
 
+def csa_index_topk_workspace_size(T: int, max_entries: int, k: int) -> int:
+    return int(load_library().csa_index_topk_workspace_size(int(T), int(max_entries), int(k)))
+
+
+def csa_index_topk(q_idx, q_idx_scale, w, k_idx, k_idx_scale, page_table, n_comp, q_pos, q_seq, ratio_m, k,
+                   topk_idx, n_visible, workspace=None, stream=None):
+    """Steps 1+2 fused: the top-k of the indexer scores without writing them."""
+    _need(q_idx, "q_idx", _U8, 3)
+    _need(w, "w", _F32, 2)
+    _need(k_idx, "k_idx", _U8, 3)
+    _need(page_table, "page_table", _I32, 2)
+    _need(n_comp, "n_comp", _I32, 1)
+    _need(q_pos, "q_pos", _I32, 1)
+    if q_seq is not None:                  # None: query t belongs to sequence t
+        _need(q_seq, "q_seq", _I32, 1)
+    _need(topk_idx, "topk_idx", _I32, 2)
+    _need(n_visible, "n_visible", _I32, 1)
+    T, H_I, D_I = q_idx.shape
+    P, ps, dk = k_idx.shape
+    if dk != D_I or tuple(w.shape) != (T, H_I) or tuple(topk_idx.shape) != (T, int(k)):
+        raise ValueError("inconsistent indexer / top-k shapes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().csa_index_topk(
+        _ptr(q_idx), float(q_idx_scale), _ptr(w), _ptr(k_idx), float(k_idx_scale), _ptr(page_table), _ptr(n_comp),
+        P, ps, page_table.shape[1], page_table.shape[0], _ptr(q_pos), _ptr(q_seq), T, H_I, D_I, int(ratio_m),
+        int(k), _ptr(topk_idx), _ptr(n_visible), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("csa_index_topk", rc)
+
+
 def csa_topk_workspace_size(T: int, ld_scores: int, k: int) -> int:
     return int(load_library().csa_topk_workspace_size(int(T), int(ld_scores), int(k)))
 
@@ -371,10 +405,12 @@ class DecodePath(_Path):
 
     def __init__(self, *, cache: LatentCache, swa: SwaRing, q, q_pos, sink, softmax_scale, k,
                  q_idx=None, q_idx_scale=1.0, w=None, k_idx=None, k_idx_scale=1.0, inv_rope_theta=0.0,
-                 q_idx_sc=None, k_idx_sc=None):
+                 q_idx_sc=None, k_idx_sc=None, fused_topk=False):
         dev = q.device
         self.inv_rope_theta = float(inv_rope_theta)
         self.q_idx_sc, self.k_idx_sc = q_idx_sc, k_idx_sc   # both given: MXFP4 indexer inputs
+        # steps 1+2 as one call that keeps the scores on chip (E4M3 only)
+        self.fused_topk = bool(fused_topk) and q_idx is not None and q_idx_sc is None
         self.cache, self.swa, self.q, self.q_pos, self.sink = cache, swa, q, q_pos, sink
         self.softmax_scale, self.k = float(softmax_scale), int(k)
         self.q_idx, self.q_idx_scale, self.w, self.k_idx, self.k_idx_scale = q_idx, q_idx_scale, w, k_idx, k_idx_scale
@@ -386,13 +422,18 @@ class DecodePath(_Path):
         self.out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         if q_idx is not None:
-            self.scores = torch.empty((B, self.ld), dtype=torch.float32, device=dev)
             self.n_vis = torch.empty((B,), dtype=torch.int32, device=dev)
             self.topk = torch.empty((B, self.k), dtype=torch.int32, device=dev)
-            tw = csa_topk_workspace_size(B, self.ld, self.k)
+            if self.fused_topk:
+                self.scores = None
+                tw = csa_index_topk_workspace_size(B, max_entries, self.k)
+                self.stage_names = ("index_topk", "decode_attn")
+            else:
+                self.scores = torch.empty((B, self.ld), dtype=torch.float32, device=dev)
+                tw = csa_topk_workspace_size(B, self.ld, self.k)
+                self.stage_names = ("index_scores", "topk", "decode_attn")
             self.topk_ws = torch.empty((max(tw, 16),), dtype=torch.uint8, device=dev) if tw else None
             max_keys = self.k + swa.pos.shape[1]
-            self.stage_names = ("index_scores", "topk", "decode_attn")
         else:
             self.scores = self.n_vis = self.topk = self.topk_ws = None
             max_keys = max_entries + swa.pos.shape[1]
@@ -409,10 +450,20 @@ class DecodePath(_Path):
             _need(self.q_idx, "q_idx", _U8, 3)
             _need(self.k_idx, "k_idx", _U8, 3)
             _need(self.w, "w", _F32, 2)
-            plan.append(self._index_stage())
             tw = 0 if self.topk_ws is None else self.topk_ws.numel()
-            plan.append(("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), B, self.k, _ptr(self.topk),
-                                      _ptr(self.topk_ws), tw)))
+            if self.fused_topk:
+                T, H_I, D_I = self.q_idx.shape
+                P, ps, _ = self.k_idx.shape
+                pt = self.cache.page_table
+                plan.append(("csa_index_topk", (
+                    _ptr(self.q_idx), float(self.q_idx_scale), _ptr(self.w), _ptr(self.k_idx),
+                    float(self.k_idx_scale), _ptr(pt), _ptr(self.cache.n_comp), P, ps, pt.shape[1], pt.shape[0],
+                    _ptr(self.q_pos), _ptr(self.q_seq), T, H_I, D_I, int(self.cache.ratio_m), self.k,
+                    _ptr(self.topk), _ptr(self.n_vis), _ptr(self.topk_ws), tw)))
+            else:
+                plan.append(self._index_stage())
+                plan.append(("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), B, self.k, _ptr(self.topk),
+                                          _ptr(self.topk_ws), tw)))
         aw = 0 if self.attn_ws is None else self.attn_ws.numel()
         plan.append(("csa_decode_attn", (
             _ptr(self.q), self.q.stride(0), ctypes.byref(self._cc), _ptr(self.topk), self.k, ctypes.byref(self._sc),

@@ -48,6 +48,24 @@ TopkPlan plan_topk(int32_t T, int64_t ld, int32_t k) {
   return pl;
 }
 
+// ---- fused indexer + top-k: chunk of entries per workgroup ----------------
+// The smallest of 2048, 4096, 8192 entries whose candidates (chunks x k) the
+// merge can take, or one chunk for the whole row.
+TopkPlan plan_index_topk(int32_t T, int64_t span, int32_t k) {
+  TopkPlan pl;
+  for (int chunk : {2048, 4096, 8192}) {
+    const int64_t n = std::max<int64_t>(1, ceil_div(span, chunk));
+    if (n == 1 || n * k <= kTopkMaxCand) {
+      pl.chunk = chunk;
+      pl.n_chunks = (int)n;
+      pl.ws_bytes = n > 1 ? (size_t)T * (size_t)n * (size_t)k * 8u : 0;
+      pl.ok = true;
+      return pl;
+    }
+  }
+  return pl;
+}
+
 // ---- attention split of the key range over workgroups ---------------------
 constexpr int kTargetBlocks = 256;   // one workgroup per CU on MI355X
 struct AttnPlan {
@@ -112,7 +130,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_LAUN
 
 extern "C" {
 
-int csa_version(void) { return 120; }
+int csa_version(void) { return 130; }
 
 const char* csa_status_string(int code) {
   switch (code) {
@@ -193,6 +211,65 @@ int csa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_idx_sc, const 
   p.qk_scale = 1.0f;
   return index_scores_common(p, page_table, n_comp, num_pages, page_size, max_pages, B, q_pos, q_seq, T, H_I, D_I,
                              ratio_m, scores, ld_scores, n_visible, stream);
+}
+
+size_t csa_index_topk_workspace_size(int32_t T, int64_t max_entries, int32_t k) {
+  if (T < 1 || max_entries < 1 || k < 1 || k > kTopkMaxK) return 0;
+  const TopkPlan pl = plan_index_topk(T, max_entries, k);
+  return pl.ok ? pl.ws_bytes : 0;
+}
+
+int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w, const uint8_t* k_idx, float k_idx_scale,
+                   const int32_t* page_table, const int32_t* n_comp, int32_t num_pages, int32_t page_size,
+                   int32_t max_pages, int32_t B, const int32_t* q_pos, const int32_t* q_seq, int32_t T, int32_t H_I,
+                   int32_t D_I, int32_t ratio_m, int32_t k, int32_t* topk_idx, int32_t* n_visible, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (T < 0) return CSA_ERR_INVALID_ARG;
+  if (T == 0) return CSA_OK;
+  if (!q_idx || !w || !k_idx || !page_table || !n_comp || !q_pos || !topk_idx || !n_visible)
+    return CSA_ERR_INVALID_ARG;
+  if (!aligned16(q_idx) || !aligned16(k_idx)) return CSA_ERR_INVALID_ARG;
+  if (B < 1 || num_pages < 1 || page_size < 16 || page_size % 16 || max_pages < 1 || ratio_m < 1)
+    return CSA_ERR_INVALID_ARG;
+  if (!(q_idx_scale > 0.0f) || !(k_idx_scale > 0.0f) || !std::isfinite(q_idx_scale) || !std::isfinite(k_idx_scale))
+    return CSA_ERR_INVALID_ARG;
+  if (H_I < 1 || H_I > 64 || !(D_I == 32 || D_I == 64 || D_I == 96 || D_I == 128)) return CSA_ERR_UNSUPPORTED;
+  if (k < 1 || k > kTopkMaxK) return CSA_ERR_UNSUPPORTED;
+  const int64_t span = (int64_t)max_pages * page_size;
+  const TopkPlan pl = plan_index_topk(T, span, k);
+  if (!pl.ok) return CSA_ERR_UNSUPPORTED;
+  if (pl.n_chunks > 1 && (!workspace || !aligned16(workspace) || workspace_bytes < pl.ws_bytes))
+    return CSA_ERR_WORKSPACE;
+  if ((int64_t)T * pl.n_chunks >= ((int64_t)1 << 31)) return CSA_ERR_UNSUPPORTED;
+  IndexParams p{};
+  p.q_idx = q_idx;
+  p.w = w;
+  p.k_idx = k_idx;
+  p.qk_scale = q_idx_scale * k_idx_scale;
+  p.page_table = page_table;
+  p.n_comp = n_comp;
+  p.q_pos = q_pos;
+  p.q_seq = q_seq;
+  p.n_visible = n_visible;
+  p.num_pages = num_pages;
+  p.page_size = page_size;
+  p.max_pages = max_pages;
+  p.B = B;
+  p.T = T;
+  p.H_I = H_I;
+  p.D_I = D_I;
+  p.ratio_m = ratio_m;
+  TopkParams tp{};
+  tp.out = topk_idx;
+  tp.T = T;
+  tp.k = k;
+  tp.chunk = pl.chunk;
+  tp.n_chunks = pl.n_chunks;
+  if (pl.n_chunks > 1) {
+    tp.cand_key = static_cast<uint32_t*>(workspace);
+    tp.cand_idx = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + pl.ws_bytes / 2);
+  }
+  return launch_status(launch_index_topk(p, tp, (hipStream_t)stream));
 }
 
 size_t csa_topk_workspace_size(int32_t T, int64_t ld_scores, int32_t k) {

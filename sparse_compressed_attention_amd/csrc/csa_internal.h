@@ -40,6 +40,12 @@ struct TopkParams {
   int chunk, n_chunks;
 };
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+// stage 2 alone: merges per-chunk candidates already in cand_key / cand_idx
+hipError_t launch_topk_merge(const TopkParams& p, hipStream_t stream);
+// fused indexer + top-k (decode kernel layout, E4M3 operands): scores stay in
+// LDS; one workgroup per (row, chunk of `chunk` entries) selects the chunk's
+// top-k, then the merge (when a row has several chunks)
+hipError_t launch_index_topk(const IndexParams& ip, const TopkParams& tp, hipStream_t stream);
 constexpr int kTopkMaxChunk = 16384;
 constexpr int kTopkMaxCand = 16384;
 constexpr int kTopkMaxK = 2048;

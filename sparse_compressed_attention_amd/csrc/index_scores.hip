@@ -24,6 +24,7 @@
 // groups with two permlane swaps.  The scan is HBM-bound (128 FLOP/byte).
 #include "csa_device.h"
 #include "csa_internal.h"
+#include "topk_select.h"
 
 #include <algorithm>
 
@@ -434,6 +435,170 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   }
 }
 
+// ---- fused indexer + top-k ------------------------------------------------
+// "DSV4 Audit", B2: score and select with a wave-local reduction and no
+// global lock.  One workgroup (8 waves) per (row, chunk of kRounds x 512
+// entries): the chunk's scores are computed as in the one-query kernel
+// (a wave scores 64 entries per round, the next round's keys in flight
+// while the current one is scored) but kept in LDS, then the workgroup
+// selects the chunk's top-k with the same radix selection as the top-k
+// kernels.  A row of one chunk gets its final answer here; longer rows
+// leave per-chunk candidates for the top-k merge.  The scores never go to
+// HBM.
+constexpr int kFtWaves = 8;
+constexpr int kFtRound = kFtWaves * 4 * 16;   // entries per round: 4 groups of 16 per wave
+
+template <int kRounds>
+__global__ __launch_bounds__(64 * kFtWaves, 1) void index_topk_kernel(IndexParams p, TopkParams tp) {
+  constexpr int kChunk = kRounds * kFtRound;
+  constexpr int kThreads = 64 * kFtWaves;
+  constexpr int SEG = kChunk / kThreads;       // keys per thread in the selection
+  static_assert(SEG == 4 || SEG == 8 || SEG == 16, "selection segment");
+  static_assert(4 * kRounds <= 64, "one page-id lane per group");
+  __shared__ __attribute__((aligned(16))) float sc[kChunk];
+  __shared__ v8i qs[4 * 64];
+  __shared__ topk_sel::TopkShared<kThreads> sh;
+  const int chunk = blockIdx.x / p.T;           // chunk-major, as the one-query kernel
+  const int t = blockIdx.x - chunk * p.T;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const bool dim_ok = 32 * g < p.D_I;
+  const int c0 = chunk * kChunk;
+
+  // ---- first round trip: query tile (waves 0-3, shared through LDS),
+  // weights, position, and the page ids of all of this wave's groups
+  // (lane 4 rd + u holds group u of round rd)
+  v8i qa[4];
+  if (wave < 4) {
+    const int h = 16 * wave + r;
+    qa[0] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    if (h < p.H_I && dim_ok) {
+      const uint8_t* src = p.q_idx + ((size_t)t * p.H_I + h) * p.D_I + 32 * g;
+      const v4i lo = ld16(src), hi = ld16(src + 16);
+      qa[0] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  v4f wv[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h0 = 16 * ht + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[ht][i] = h0 + i < p.H_I ? p.w[(size_t)t * p.H_I + h0 + i] : 0.0f;
+  }
+  const int seq = p.q_seq ? p.q_seq[t] : t;
+  const int pos = p.q_pos[t];
+  const bool seq_ok = seq >= 0 && seq < p.B;
+  int my_page = -1;
+  if (seq_ok && lane < 4 * kRounds) {
+    const int rd = lane >> 2, u = lane & 3;
+    const int pi = (c0 + rd * kFtRound + wave * 64 + 16 * u) / p.page_size;
+    if (pi < p.max_pages) my_page = p.page_table[(size_t)seq * p.max_pages + pi];
+  }
+  int nv = 0;
+  if (seq_ok && pos >= 0) nv = min(pos / p.ratio_m, p.n_comp[seq]);
+  nv = max(0, nv);
+  if (chunk == 0 && threadIdx.x == 0) p.n_visible[t] = nv;
+  const int n = max(0, min(kChunk, nv - c0));   // visible entries of this chunk (uniform)
+
+  // keys of round rd for this wave: group u covers entries
+  // c0 + rd * kFtRound + 64 wave + 16 u + (0..15)
+  auto load_round = [&](int rd, v8i (&kb)[4], uint32_t& okm) {
+    okm = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int le = rd * kFtRound + wave * 64 + 16 * u;   // chunk-local first entry
+      const int page = __builtin_amdgcn_readlane(my_page, 4 * rd + u);
+      const bool ok = le < n && page >= 0 && page < p.num_pages;
+      okm |= (ok ? 1u : 0u) << u;
+      v8i x = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+      if (ok && dim_ok && le + r < n) {
+        const int poff = (c0 + le) % p.page_size;
+        const uint8_t* src = p.k_idx + ((size_t)page * p.page_size + poff + r) * p.D_I + 32 * g;
+        const v4i lo = ld16(src), hi = ld16(src + 16);
+        x = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      kb[u] = x;
+    }
+  };
+  v8i kb[2][4];
+  uint32_t okm[2];
+  load_round(0, kb[0], okm[0]);
+  if (wave < 4) qs[wave * 64 + lane] = qa[0];
+  lds_barrier();
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) qa[ht] = qs[ht * 64 + lane];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) wv[ht] *= p.qk_scale;
+
+  auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = mfma_f8_128(qa[ht], k, (v4f){0.f, 0.f, 0.f, 0.f});
+  };
+#pragma unroll
+  for (int rd = 0; rd < kRounds; ++rd) {
+    const int cur = rd & 1;
+    if (rd + 1 < kRounds) load_round(rd + 1, kb[cur ^ 1], okm[cur ^ 1]);
+    const int le0 = rd * kFtRound + wave * 64;
+    if (le0 < n) {
+      v4f acc[2][4];
+      float xg[4];
+      mfmas(kb[cur][0], acc[0]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u + 1 < 4) mfmas(kb[cur][u + 1], acc[(u + 1) & 1]);
+        xg[u] = wrelu16(acc[u & 1], wv);
+      }
+      // lane (g, r) now holds entry r of group g
+      const float tot = reduce4_scatter(xg[0], xg[1], xg[2], xg[3]);
+      const int le = le0 + 16 * g + r;
+      if (le < n) sc[le] = ((okm[cur] >> g) & 1u) ? tot : -__builtin_inff();
+    }
+  }
+  __syncthreads();   // the chunk's scores are in LDS
+
+  // ---- selection over the chunk (thread i: scores [SEG i, SEG i + SEG))
+  const int i0 = threadIdx.x * SEG;
+  uint32_t key[SEG];
+#pragma unroll
+  for (int j = 0; j < SEG; j += 4) {
+    const v4f v = *reinterpret_cast<const v4f*>(sc + i0 + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[j + e] = float_order_key(v[e]);
+  }
+  const int cnt = max(0, min(SEG, n - i0));
+  const uint32_t valid = cnt >= 32 ? 0xffffffffu : ((1u << cnt) - 1u);
+  const int K = min(tp.k, n);
+  if (tp.n_chunks == 1) {
+    int32_t* o = tp.out + (size_t)t * tp.k;
+    if (K > 0) {
+      const topk_sel::Sel s = topk_sel::radix_select<kThreads, SEG>(key, valid, K, sh);
+      topk_sel::emit_selected<kThreads, SEG>(key, valid, s, sh, [&](int rank, int j) {
+        if (rank < K) o[rank] = c0 + i0 + j;
+      });
+    }
+    for (int i = K + threadIdx.x; i < tp.k; i += kThreads) o[i] = -1;
+  } else {
+    const size_t base = ((size_t)t * tp.n_chunks + chunk) * tp.k;
+    uint32_t* ck = tp.cand_key + base;
+    int32_t* ci = tp.cand_idx + base;
+    if (K > 0) {
+      const topk_sel::Sel s = topk_sel::radix_select<kThreads, SEG>(key, valid, K, sh);
+      topk_sel::emit_selected<kThreads, SEG>(key, valid, s, sh, [&](int rank, int j) {
+        if (rank < K) {
+          ck[rank] = key[j];
+          ci[rank] = c0 + i0 + j;
+        }
+      });
+    }
+    for (int i = K + threadIdx.x; i < tp.k; i += kThreads) {
+      ck[i] = 0u;
+      ci[i] = -1;
+    }
+  }
+}
+
 template <int kWaves, int kGroups, int kOcc, bool kQLds, bool kFp4>
 hipError_t launch_decode(IndexParams p, int64_t span, hipStream_t stream) {
   constexpr int kChunk = kWaves * kGroups * 16;
@@ -471,6 +636,29 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
   // the same bytes in flight)
   if (p.fp4) return launch_decode<4, 8, 4, true, true>(p, span, stream);
   return launch_decode<4, 4, 4, true, false>(p, span, stream);
+}
+
+hipError_t launch_index_topk(const IndexParams& p_in, const TopkParams& tp_in, hipStream_t stream) {
+  IndexParams p = p_in;
+  TopkParams tp = tp_in;
+  const int64_t blocks = (int64_t)p.T * tp.n_chunks;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  switch (tp.chunk) {
+    case 4 * kFtRound:
+      hipLaunchKernelGGL(index_topk_kernel<4>, dim3((unsigned)blocks), dim3(64 * kFtWaves), 0, stream, p, tp);
+      break;
+    case 8 * kFtRound:
+      hipLaunchKernelGGL(index_topk_kernel<8>, dim3((unsigned)blocks), dim3(64 * kFtWaves), 0, stream, p, tp);
+      break;
+    case 16 * kFtRound:
+      hipLaunchKernelGGL(index_topk_kernel<16>, dim3((unsigned)blocks), dim3(64 * kFtWaves), 0, stream, p, tp);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess || tp.n_chunks == 1) return e;
+  return launch_topk_merge(tp, stream);
 }
 
 }  // namespace csa

@@ -217,6 +217,61 @@ def test_inverse_rope_full_size(name, queries, theta):
     check_full(ci.make_config(name), queries=queries, inv_rope_theta=theta)
 
 
+# --------------------------------------------------------------- fused indexer + top-k
+@pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "tiny_dims_wide", "poisoned", "c1", "c2",
+                                  "c3_csa"])
+def test_fused_index_topk_equals_two_calls(case):
+    # the fused call computes the same scores (same MFMA order) and applies
+    # the same selection, so its indices are bit-identical to
+    # csa_index_scores + csa_topk; they are also gated against the oracle
+    say(f"case fused indexer + top-k {case}")
+    qs = None
+    if case in ("c0", "c1", "c2", "c3_csa"):
+        wl = ci.make_config(case)
+        qs = {"c2": [0, 31, 63], "c3_csa": [1, 3]}.get(case)
+    elif case == "small_ragged":
+        wl = ci.generate(ci.small_spec(shuffle_pages=True), seed=171)
+    elif case == "many_sequences":
+        spec = ci.small_spec(ctx_lens=[4096, 2052, 2500, 3332, 1028, 4100, 2600, 9000], shuffle_pages=True, k=384)
+        wl = ci.generate(spec, seed=172)
+    elif case == "tiny_dims_wide":
+        rng = np.random.default_rng(173)
+        lens = [int(x) * 4 for x in rng.integers(40, 160, size=300)]
+        spec = ci.Spec(name="tiny_decode_300", kind="decode", ctx_lens=lens, H=8, D_nope=48, D_rope=16, H_I=4,
+                       D_I=32, k=16, W=32, page_size=16, shuffle_pages=True)
+        wl, qs = ci.generate(spec, seed=173), [0, 1, 150, 299]
+    else:
+        # own and future blocks made the strongest keys: never selected
+        wl = ci.generate(ci.small_spec(ctx_lens=[3000, 2400], shuffle_pages=True), seed=174)
+        s = wl.spec
+        k_idx = wl.k_idx.copy()
+        for b in range(wl.B):
+            nv = oracle.n_visible(int(wl.q_pos[b]), s.m, int(wl.n_comp[b]))
+            for c in range(nv, int(wl.n_comp[b])):
+                page = int(wl.page_table[b][c // s.page_size])
+                k_idx[page, c % s.page_size] = wl.q_idx[b][0]
+        wl = dataclasses.replace(wl, k_idx=k_idx)
+    d = to_device(wl, "cuda")
+    two = make_path(d)
+    fused = make_path(d, fused_topk=True)
+    assert fused.stage_names == ("index_topk", "decode_attn")
+    two.run()
+    fused.run()
+    torch.cuda.synchronize()
+    assert torch.equal(two.topk, fused.topk)
+    assert torch.equal(two.n_vis, fused.n_vis)
+    assert torch.equal(two.out.view(torch.int16), fused.out.view(torch.int16))
+    topk = fused.topk.cpu().numpy()
+    exact = 0
+    for t in (range(wl.T) if qs is None else qs):
+        ref_scores = oracle.index_scores(wl, t)
+        exact += P.check_topk_vs_oracle(topk[t], ref_scores, wl.spec.k)
+        if case == "poisoned":
+            nv = oracle.n_visible(int(wl.q_pos[t]), wl.spec.m, int(wl.n_comp[int(wl.q_seq[t])]))
+            assert (topk[t] < nv).all()
+    say(f"  {case}: fused == two calls; exact top-k sets vs oracle {exact}")
+
+
 # --------------------------------------------------------------- MXFP4 indexer
 @pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "prefill_small", "tiny_dims_wide",
                                   "heads40_dims64", "heads24_dims96_prefill"])
