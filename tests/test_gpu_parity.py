@@ -256,11 +256,15 @@ def test_fused_index_topk_equals_two_calls(case):
     fused = make_path(d, fused_topk=True)
     assert fused.stage_names == ("index_topk", "decode_attn")
     two.run()
-    fused.run()
-    torch.cuda.synchronize()
-    assert torch.equal(two.topk, fused.topk)
-    assert torch.equal(two.n_vis, fused.n_vis)
-    assert torch.equal(two.out.view(torch.int16), fused.out.view(torch.int16))
+    # three calls in a row on one (zero-filled) workspace: the arrival
+    # counters of long rows must be back at zero after every call
+    for rep in range(3):
+        fused.topk.fill_(-7)
+        fused.run()
+        torch.cuda.synchronize()
+        assert torch.equal(two.topk, fused.topk), f"call {rep}"
+        assert torch.equal(two.n_vis, fused.n_vis)
+        assert torch.equal(two.out.view(torch.int16), fused.out.view(torch.int16))
     topk = fused.topk.cpu().numpy()
     exact = 0
     for t in (range(wl.T) if qs is None else qs):
