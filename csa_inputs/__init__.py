@@ -93,6 +93,7 @@ class Spec:
     unit_scale: bool = False       # values already on the E4M3 grid (scale 1)
     with_indexer: bool = True      # False for the HCA layer (no indexer inputs)
     mxfp4: bool = False            # also store the indexer q/k in MXFP4 (same draws)
+    keep_float: bool = False       # also keep the indexer q/k draws unquantised (float32)
     # prefill only: number of query tokens at the end of the single sequence
     T_prefill: int = 0
     # decode: position of each sequence's query (default ctx_len - 1)
@@ -124,6 +125,11 @@ class Workload:
     q_idx4_sc: Optional[np.ndarray] = None # u8 [T][H_I][D_I/32]
     k_idx4: Optional[np.ndarray] = None    # u8 [P][ps][D_I/2]
     k_idx4_sc: Optional[np.ndarray] = None # u8 [P][ps][D_I/32]
+    # the unquantised indexer draws (spec.keep_float): q [T][H_I][D_I], and
+    # the keys in entry order [sum n_comp][D_I], sequence b's from entry_offset[b]
+    q_idx_f32: Optional[np.ndarray] = None
+    k_idx_f32: Optional[np.ndarray] = None
+    entry_offset: Optional[np.ndarray] = None
     # compressed latent cache
     lat_nope: np.ndarray = None            # u8 [P][ps][D_nope]
     lat_rope: np.ndarray = None            # u16 [P][ps][D_rope]
@@ -196,6 +202,8 @@ def generate(spec: Spec, seed: int) -> Workload:
         wl.q_idx = e4m3_bytes(qi, wl.q_idx_scale)
         if s.mxfp4:
             wl.q_idx4, wl.q_idx4_sc = mxfp4_pack(qi)
+        if s.keep_float:
+            wl.q_idx_f32 = qi
         del qi
         wl.w = rng.random((T, s.H_I), dtype=np.float32)
         ki = _draw_normal(rng, (n_entries, s.D_I))
@@ -203,6 +211,9 @@ def generate(spec: Spec, seed: int) -> Workload:
         ki_b = e4m3_bytes(ki, wl.k_idx_scale)
         if s.mxfp4:
             ki4, ki4_sc = mxfp4_pack(ki)
+        if s.keep_float:
+            wl.k_idx_f32 = ki
+            wl.entry_offset = np.concatenate([[0], np.cumsum(n_comp)[:-1]]).astype(np.int64)
         del ki
     # ---- compressed latents
     lat = _draw_normal(rng, (n_entries, s.D))

@@ -33,4 +33,5 @@ from .codecs import e4m3_decode, bf16_decode, e2m1_decode, e8m0_decode, mxfp4_de
 from .csa import (  # noqa: F401
     n_visible, index_scores, topk_select, key_rows, attend, run_decode_path,
     run_attention, merge_by_lse, dequant_entries, entry_rows, inverse_rope, index_scores_mxfp4,
+    index_scores_unquantised,
 )

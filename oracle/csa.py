@@ -79,6 +79,21 @@ def index_scores_mxfp4(wl, t: int, keys: np.ndarray | None = None) -> np.ndarray
     return w @ np.maximum(logits, 0.0)
 
 
+def index_scores_unquantised(wl, t: int) -> np.ndarray:
+    """The indexer scores of index_scores() on the draws before any
+    quantisation (spec.keep_float): the reference against which [Roadmap] E7
+    measures an indexer's recall ("recall vs the FP32 oracle").  Same
+    formula; only the inputs differ."""
+    s = wl.spec
+    b = int(wl.q_seq[t])
+    nv = n_visible(int(wl.q_pos[t]), s.m, int(wl.n_comp[b]))
+    off = int(wl.entry_offset[b])
+    keys = wl.k_idx_f32[off:off + nv].astype(np.float64)
+    q = wl.q_idx_f32[t].astype(np.float64)
+    w = wl.w[t].astype(np.float64)
+    return w @ np.maximum(q @ keys.T, 0.0)
+
+
 def index_scores(wl, t: int, keys: np.ndarray | None = None) -> np.ndarray:
     """Indexer scores of query t over its visible entries, float64 [n_vis].
 

@@ -10,6 +10,9 @@ E7).  CPU only.
    of 32 dims.
  * Scores: a pure-Python loop over the decoded values on a tiny workload, and
    the FP8 scores themselves when the MXFP4 copy holds the same values.
+ * Unquantised reference scores (the recall reference of "ROADMAP", E7): the
+   E4M3 scores exactly when the kept draws are replaced by their E4M3 values,
+   and the kept draws round to the stored bytes.
 """
 import dataclasses
 import math
@@ -120,3 +123,30 @@ def test_mxfp4_scores_track_fp8_scores_on_random_data():
     a = oracle.index_scores(wl, 0)
     b = oracle.index_scores_mxfp4(wl, 0)
     assert np.corrcoef(a, b)[0, 1] > 0.95
+
+
+def test_unquantised_scores_equal_fp8_scores_when_the_draws_are_on_the_grid():
+    # replace the kept float draws by their E4M3-decoded values: the
+    # unquantised scores must then be the E4M3 scores exactly
+    spec = ci.Spec(name="tiny_float", kind="decode", ctx_lens=[256, 200], H=8, D_nope=48, D_rope=16, H_I=4, D_I=32,
+                   k=16, W=32, page_size=16, shuffle_pages=True, keep_float=True)
+    wl = ci.generate(spec, 12)
+    from oracle.codecs import e4m3_decode
+    q = e4m3_decode(wl.q_idx) * wl.q_idx_scale
+    keys = np.zeros_like(wl.k_idx_f32, dtype=np.float64)
+    s = wl.spec
+    for b in range(wl.B):
+        for c in range(int(wl.n_comp[b])):
+            page = int(wl.page_table[b][c // s.page_size])
+            keys[int(wl.entry_offset[b]) + c] = e4m3_decode(wl.k_idx[page, c % s.page_size]) * wl.k_idx_scale
+    wl2 = dataclasses.replace(wl, q_idx_f32=q, k_idx_f32=keys)
+    for t in range(wl.T):
+        assert np.allclose(oracle.index_scores_unquantised(wl2, t), oracle.index_scores(wl, t), rtol=1e-13, atol=1e-13)
+
+
+def test_unquantised_draws_are_the_quantised_ones_before_rounding():
+    # the kept draws round to the stored E4M3 bytes (the same draw order)
+    spec = ci.Spec(name="tiny_float2", kind="decode", ctx_lens=[256], H=8, D_nope=48, D_rope=16, H_I=4, D_I=32,
+                   k=16, W=32, page_size=16, keep_float=True)
+    wl = ci.generate(spec, 13)
+    assert np.array_equal(ci.e4m3_bytes(wl.q_idx_f32, wl.q_idx_scale), wl.q_idx)
