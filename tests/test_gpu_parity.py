@@ -106,6 +106,36 @@ def test_prefill_small():
     check_full(ci.generate(spec, seed=104), queries=[0, 1, 17, 33, 50, 69])
 
 
+@pytest.mark.parametrize("T", [40, 300])
+def test_prefill_hca_mode(T):
+    # csa_prefill_attn with no top-k list: every visible entry of an m'=128
+    # cache plus the window from the linear buffer (few queries: split key
+    # ranges and the merge; 300 queries: 64-head workgroups, no split)
+    say(f"case prefill HCA ({T} queries)")
+    spec = ci.Spec(name=f"prefill_hca_{T}", kind="prefill", ctx_lens=[60000], T_prefill=T, m=128,
+                   with_indexer=False)
+    wl = ci.generate(spec, seed=119 + T)
+    s = wl.spec
+    d = to_device(wl, "cuda")
+    cache = csa.LatentCache(d.lat_nope, d.lat_rope, d.lat_scale, d.page_table, d.n_comp, s.m)
+    max_keys = d.page_table.shape[1] * d.lat_nope.shape[1] + s.W
+    ws_bytes = csa.csa_attn_workspace_size(T, s.H, s.D_nope, s.D_rope, max_keys)
+    ws = torch.zeros((max(ws_bytes, 16),), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, s.H, s.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, s.H), dtype=torch.float32, device="cuda")
+    csa.csa_prefill_attn(d.q, cache, 0, None, 0, d.swa_nope, d.swa_rope, d.swa_scale, d.swa_first_pos, s.W,
+                         d.q_pos, d.sink, s.sigma, out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    lv = lse.cpu().numpy().astype(np.float64)
+    worst = (0.0, 1.0)
+    for t in ([0, T // 2, T - 1]):
+        o_ref, l_ref = P.reference_attention_on(wl, t, None)
+        err, cos = P.check_attention(o[t], lv[t], o_ref, l_ref)
+        worst = (max(worst[0], err), min(worst[1], cos))
+    say(f"  max|err| {worst[0]:.3e} min cos {worst[1]:.6f}")
+
+
 def test_prefill_64_head_workgroups():
     # 160 queries x 2 groups of 64 heads fill the GPU without splitting the
     # key range, so the launch uses 64-head (8-wave) workgroups
