@@ -382,6 +382,40 @@ def test_mxfp4_indexer_full_size(name, queries):
     check_full(ci.make_config(name, mxfp4=True), queries=queries, mxfp4=True)
 
 
+@pytest.mark.parametrize("k", [1, 2048])
+def test_decode_extreme_k(k):
+    # k = 1 (one selected entry) and k = 2048 (the largest; more slots than
+    # one workgroup takes, and more than some rows have visible entries)
+    say(f"case decode k={k}")
+    spec = ci.small_spec(name=f"small_k{k}", ctx_lens=[12000, 3000, 620], k=k, shuffle_pages=True)
+    check_full(ci.generate(spec, seed=180 + k))
+
+
+def test_decode_fewer_queries_than_cached_sequences():
+    # B = 2 queries against a cache of 4 sequences: query b is sequence b
+    say("case decode B < cached sequences")
+    wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1508, 2400, 700], shuffle_pages=True), seed=185)
+    s = wl.spec
+    d = to_device(wl, "cuda")
+    B = 2
+    cache = csa.LatentCache(d.lat_nope, d.lat_rope, d.lat_scale, d.page_table, d.n_comp, s.m)
+    swa = csa.SwaRing(d.swa_nope, d.swa_rope, d.swa_scale, d.swa_pos)
+    path = csa.DecodePath(cache=cache, swa=swa, q=d.q[:B].contiguous(), q_pos=d.q_pos[:B].contiguous(),
+                          sink=d.sink, softmax_scale=s.sigma, k=s.k, q_idx=d.q_idx[:B].contiguous(),
+                          q_idx_scale=d.q_idx_scale, w=d.w[:B].contiguous(), k_idx=d.k_idx,
+                          k_idx_scale=d.k_idx_scale)
+    out, lse = path.run()
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    lv = lse.cpu().numpy().astype(np.float64)
+    topk = path.topk.cpu().numpy()
+    for t in range(B):
+        P.check_topk_vs_oracle(topk[t], oracle.index_scores(wl, t), s.k)
+        o_ref, l_ref = P.reference_attention_on(wl, t, topk[t])
+        err, cos = P.check_attention(o[t], lv[t], o_ref, l_ref)
+        say(f"  query {t}: max|err| {err:.3e} min cos {cos:.6f}")
+
+
 def test_ring_permutation_invariance_gpu():
     say("case ring permutation")
     wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1800]), seed=105)
