@@ -10,7 +10,9 @@ from .codecs import e4m3_decode, bf16_decode
 
 
 def brute_path(wl, t):
-    """Scores, selection, and (o, lse) of query t by explicit loops."""
+    """Scores, selection, and (o, lse) of query t by explicit loops, for a
+    decode batch (window rows from the ring) or a prefill chunk (window rows
+    from the linear token buffer, every query at its own position)."""
     s = wl.spec
     b = int(wl.q_seq[t])
     pos = int(wl.q_pos[t])
@@ -45,10 +47,19 @@ def brute_path(wl, t):
 
     X = [row(nflat[phys(c)], rflat[phys(c)], wl.lat_scale) for c in chosen]
     lo = max(0, pos - s.W + 1)
-    for j in range(s.W):
-        p = int(wl.swa_pos[b][j])
-        if lo <= p <= pos:
-            X.append(row(wl.swa_nope[b][j], wl.swa_rope[b][j], wl.swa_scale))
+    if s.kind == "decode":
+        # ring: every slot carries the position it holds
+        for j in range(s.W):
+            p = int(wl.swa_pos[b][j])
+            if lo <= p <= pos:
+                X.append(row(wl.swa_nope[b][j], wl.swa_rope[b][j], wl.swa_scale))
+    else:
+        # linear buffer of a prefill chunk: walk its rows in storage order;
+        # row j holds the token at position swa_first_pos + j
+        for j in range(int(wl.swa_len)):
+            p = int(wl.swa_first_pos) + j
+            if lo <= p <= pos:
+                X.append(row(wl.swa_nope[j], wl.swa_rope[j], wl.swa_scale))
     q = [[float(v) for v in bf16_decode(wl.q[t][h])] for h in range(s.H)]
     o, lse = [], []
     for h in range(s.H):

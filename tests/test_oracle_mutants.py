@@ -1,6 +1,8 @@
 """Each pin must catch a plausible mistake in the oracle.  Mistakes are
 planted in the oracle (on the CPU, by monkeypatching) and the matching pin
 test is expected to fail."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -81,3 +83,28 @@ def test_value_without_rope_dims_is_caught(monkeypatch):
 def test_window_excluding_own_token_is_caught(monkeypatch):
     monkeypatch.setattr(oc, "swa_window", lambda pos, W: (max(0, pos - W), pos - 1))
     _expect_fail(pins.test_window_and_newest_block_both_attended)
+
+
+def test_prefill_buffer_row_off_by_one_is_caught(monkeypatch):
+    # the window row of position p read from buffer row p - first + 1
+    real = oc.key_rows
+
+    def shifted(wl, t, sel):
+        if wl.spec.kind != "prefill":
+            return real(wl, t, sel)
+        w2 = dataclasses.replace(wl, swa_nope=np.roll(wl.swa_nope, -1, axis=0),
+                                 swa_rope=np.roll(wl.swa_rope, -1, axis=0))
+        return real(w2, t, sel)
+    monkeypatch.setattr(oc, "key_rows", shifted)
+    _expect_fail(lambda: pins.test_oracle_matches_brute_force_prefill(pins.prefill_tiny_spec))
+
+
+def test_entry_offset_of_later_sequences_is_caught(monkeypatch):
+    # the kept draws of sequence b > 0 read from the wrong offset
+    real = oc.index_scores_unquantised
+
+    def bad(wl, t):
+        w2 = dataclasses.replace(wl, entry_offset=wl.entry_offset + (np.arange(wl.B) > 0))
+        return real(w2, t)
+    monkeypatch.setattr(oracle, "index_scores_unquantised", bad)
+    _expect_fail(pins.test_unquantised_scores_against_loops_without_entry_offsets)

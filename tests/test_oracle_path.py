@@ -61,6 +61,69 @@ def test_oracle_matches_brute_force(spec_fn):
         np.testing.assert_allclose(res["lse"][t], np.array(lse), rtol=1e-12, atol=1e-12)
 
 
+def prefill_tiny_spec(**kw):
+    base = dict(name="pf_tiny", kind="prefill", ctx_lens=[203], T_prefill=9, H=5, D_nope=24, D_rope=8,
+                H_I=3, D_I=16, k=5, W=6, m=4, page_size=8, shuffle_pages=True)
+    base.update(kw)
+    return ci.Spec(**base)
+
+
+@pytest.mark.parametrize("spec_fn", [
+    prefill_tiny_spec,
+    # a chunk at the start of a sequence: early queries' windows reach below
+    # position 0, and fewer than k entries are visible
+    lambda: prefill_tiny_spec(ctx_lens=[14], T_prefill=11, k=7),
+    # a window wider than the chunk's lead-in, pages of 16
+    lambda: prefill_tiny_spec(ctx_lens=[150], T_prefill=4, W=9, page_size=16),
+])
+def test_oracle_matches_brute_force_prefill(spec_fn):
+    """The prefill path (window rows from the linear token buffer, every
+    query at its own position, all queries on one sequence's paged cache)
+    against the brute force, which walks the buffer rows in storage order
+    instead of mapping window positions to rows."""
+    wl = ci.generate(spec_fn(), seed=23)
+    assert wl.spec.kind == "prefill" and wl.T > 1
+    res = oracle.run_decode_path(wl)
+    for t in range(wl.T):
+        scores, chosen, o, lse = brute_path(wl, t)
+        np.testing.assert_allclose(res["scores"][t], scores, rtol=1e-12, atol=1e-12)
+        sel = res["topk"][t]
+        assert sel[: len(chosen)].tolist() == chosen
+        assert np.all(sel[len(chosen):] == -1)
+        np.testing.assert_allclose(res["o"][t], np.array(o), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][t], np.array(lse), rtol=1e-12, atol=1e-12)
+
+
+def test_unquantised_scores_against_loops_without_entry_offsets():
+    """index_scores_unquantised on two sequences of different lengths against
+    Python loops that find each entry's unquantised key by the E4M3 bytes
+    stored at the entry's paged row (not through the per-sequence offsets of
+    the kept draws)."""
+    spec = ci.Spec(name="uq", kind="decode", ctx_lens=[96, 181], H=4, D_nope=16, D_rope=16, H_I=3, D_I=16,
+                   k=4, W=8, page_size=16, shuffle_pages=True, keep_float=True)
+    wl = ci.generate(spec, seed=29)
+    s = wl.spec
+    enc = ci.e4m3_bytes(wl.k_idx_f32, wl.k_idx_scale)
+    lookup = {enc[i].tobytes(): i for i in range(enc.shape[0])}
+    assert len(lookup) == enc.shape[0]          # every key row has distinct bytes
+    for t in range(wl.T):
+        b = int(wl.q_seq[t])
+        nv = min(int(wl.q_pos[t]) // s.m, int(wl.n_comp[b]))
+        got = oracle.index_scores_unquantised(wl, t)
+        assert len(got) == nv
+        for c in range(nv):
+            page = int(wl.page_table[b][c // s.page_size])
+            key = wl.k_idx_f32[lookup[wl.k_idx[page, c % s.page_size].tobytes()]]
+            tot = 0.0
+            for h in range(s.H_I):
+                d = 0.0
+                for i in range(s.D_I):
+                    d += float(wl.q_idx_f32[t][h][i]) * float(key[i])
+                if d > 0.0:
+                    tot += float(wl.w[t][h]) * d
+            assert math.isclose(got[c], tot, rel_tol=1e-12, abs_tol=1e-12), (t, c, got[c], tot)
+
+
 # ------------------------------------------------------------------ golden closed forms
 def _num(v):
     table = {"ln2": math.log(2), "ln4": math.log(4), "ln3": math.log(3),
