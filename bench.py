@@ -13,10 +13,14 @@ oracle timed on a bounded sample of the same workload.  Inputs are rotated
 over several device copies so that every step reads HBM, not the 256 MB
 Infinity Cache.
 
-Two timed regions: the throughput comes from K whole steps back to back with
-no event between the kernels (an event record between two kernels adds a
-few microseconds of idle GPU); the per-kernel durations come from a second
-region that launches each stage K times back to back between two events.
+Timed regions: the throughput comes from K whole steps back to back with no
+event between the kernels (an event record between two kernels adds a few
+microseconds of idle GPU); the per-kernel durations come from a second
+region that launches each stage K times back to back between two events; a
+third region brackets every step with events for the spread of step times
+(median, p10, p90).  The roofline fractions are given against MI355X's
+published peaks and against peaks measured on the same GPU by a plain copy
+kernel and an FP8 MFMA loop (libcsa_peak.so).
 """
 from __future__ import annotations
 
@@ -58,7 +62,9 @@ def parse():
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle's CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copies", type=int, default=0, help="device copies of the inputs (0 = enough for 1 GB)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="device copies of the inputs (0 = enough that one pass over them touches >= 1 GiB)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / MFMA peaks")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured graph (csa_graph_*) instead of issuing its calls")
     ap.add_argument("--mxfp4", action="store_true",
@@ -73,16 +79,89 @@ def parse():
 
 
 def calibrate_copy(mib):
-    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counter
-    readings give the factor between those counters and bytes moved."""
+    """The plain copy probe of libcsa_peak.so over a buffer of known size,
+    launched 5 times: its FETCH_SIZE / WRITE_SIZE counter readings give the
+    factor between those counters and the bytes a kernel moves."""
+    import ctypes
     import torch
-    n = mib * (1 << 20) // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    from sparse_compressed_attention_amd import build as csa_build
+    lib = ctypes.CDLL(csa_build.PEAK_LIB_PATH)
+    lib.csa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    nbytes = mib * (1 << 20)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for _ in range(5):
-        dst.copy_(src)
+        if lib.csa_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, 256 * 16, st):
+            raise RuntimeError("csa_peak_copy failed")
     torch.cuda.synchronize()
-    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}), flush=True)
+    print(json.dumps({"calibrate_copy_bytes_read": nbytes, "calibrate_copy_bytes_written": nbytes}), flush=True)
+
+
+# --------------------------------------------------------------- measured peaks
+def measured_peaks(torch, stream, reps=5):
+    """Copy bandwidth and FP8 MFMA rate measured on this GPU (median of
+    `reps` timed launches each, after a warm-up launch), with the probes of
+    libcsa_peak.so: a 16-byte-load grid-stride copy of 2 GiB (1 GiB read +
+    1 GiB written, far beyond the 256 MB Infinity Cache) and a loop of
+    independent v_mfma_scale_f32_16x16x128_f8f6f4 on every SIMD."""
+    import ctypes
+    import numpy as np
+    from sparse_compressed_attention_amd import build as csa_build
+    lib = ctypes.CDLL(csa_build.PEAK_LIB_PATH)
+    lib.csa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    lib.csa_peak_mfma_fp8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.csa_peak_mfma_chains.restype = ctypes.c_int
+    st = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    blocks = 256 * 16
+
+    def copy():
+        if lib.csa_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, blocks, st):
+            raise RuntimeError("csa_peak_copy failed")
+    t_copy = timed(copy)
+    if not torch.equal(src[:1024], dst[:1024]):
+        raise RuntimeError("copy probe produced wrong bytes")
+    del src, dst
+    mblocks, iters = 256 * 8, 2048
+    out = torch.empty(mblocks * 256, dtype=torch.float32, device="cuda:0")
+
+    def mfma():
+        if lib.csa_peak_mfma_fp8(ctypes.c_void_p(out.data_ptr()), iters, mblocks, st):
+            raise RuntimeError("csa_peak_mfma_fp8 failed")
+    t_mfma = timed(mfma)
+    flops = mblocks * 4 * iters * lib.csa_peak_mfma_chains() * 2 * 16 * 16 * 128
+    return dict(copy_GBps=round(2 * nbytes / t_copy / 1e9, 1), fp8_mfma_TFLOPs=round(flops / t_mfma / 1e12, 1),
+                how=f"copy: {blocks} x 256 threads over 1 GiB -> 1 GiB, median of {reps}; MFMA: {mblocks} x 4 "
+                    f"waves x {iters} x {lib.csa_peak_mfma_chains()} independent 16x16x128 FP8, median of {reps}")
+
+
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count(), len(os.sched_getaffinity(0))
 
 
 # --------------------------------------------------------------- accounting
@@ -134,16 +213,28 @@ def accounting(wl, mxfp4=False):
     return acc
 
 
-def roofline_entry(name, a, ms):
+def roofline_entry(name, a, ms, peaks=None):
+    """Roofline of one kernel: algorithmic bytes (or FLOPs) per launch over
+    its average duration, against MI355X's published peak (`frac`) and, when
+    given, the peak measured on this GPU (`frac_measured`)."""
     sec = ms * 1e-3
     intensity = a["flops"] / max(a["bytes"], 1)
     gbs = a["bytes"] / sec / 1e9
     tfl = a["flops"] / sec / 1e12
     if a["flops"] > 0 and intensity >= RIDGE:
-        return dict(bound="mfma", achieved=round(tfl, 2), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
-                    frac=round(tfl / PEAK_FP8_TFLOPS, 4))
-    return dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                frac=round(gbs / PEAK_HBM_GBS, 4))
+        e = dict(bound="mfma", achieved=round(tfl, 2), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                 frac=round(tfl / PEAK_FP8_TFLOPS, 4))
+        if peaks:
+            e["peak_measured"] = peaks["fp8_mfma_TFLOPs"]
+            e["frac_measured"] = round(tfl / peaks["fp8_mfma_TFLOPs"], 4)
+        return e
+    e = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
+    if peaks:
+        e["peak_measured"] = peaks["copy_GBps"]
+        e["frac_measured"] = round(gbs / peaks["copy_GBps"], 4)
+    if a["flops"] > 0:
+        e["mfma_frac"] = round(tfl / PEAK_FP8_TFLOPS, 4)
+    return e
 
 
 def kernel_source_sha(name):
@@ -174,43 +265,52 @@ def measured_traffic(workload, name):
 
 # --------------------------------------------------------------- CPU oracle leg
 def cpu_baseline(wl, gpu_res, seconds, is_prefill, inv_rope_theta=0.0):
+    """The FP64 oracle timed on this host over a bounded sample of the
+    workload's queries (random order; stops once `seconds` have elapsed).
+    Only the oracle's own path is inside the clock; its results then check
+    the GPU's outputs, outside the clock."""
     import numpy as np
     import oracle
     from tests import parity as P
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001 - informational only
-        cores = len(os.sched_getaffinity(0))
+        blas_threads = None
+    model, n_cpu, n_aff = cpu_info()
     order = list(range(wl.T))
     rng = np.random.default_rng(0)
     rng.shuffle(order)
     done = []
-    errs = []
     t0 = time.perf_counter()
-    overlap = []
     for t in order:
-        res = oracle.run_decode_path(wl, queries=[t]) if wl.q_idx is not None else None
-        if res is not None:
+        if wl.q_idx is not None:
+            done.append((t, oracle.run_decode_path(wl, queries=[t])))
+        else:
+            done.append((t, oracle.run_attention(wl, None, queries=[t])))
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    errs, overlap = [], []
+    for t, res in done:
+        if wl.q_idx is not None:
             o_ref, l_ref = P.reference_attention_on(wl, t, gpu_res["topk"][t])
             ref_set = set(int(i) for i in res["topk"][0] if i >= 0)
             got = set(int(i) for i in gpu_res["topk"][t] if i >= 0)
             overlap.append(len(ref_set & got) / max(1, len(ref_set)))
         else:
-            o_ref, l_ref = oracle.run_attention(wl, None, queries=[t])
-            o_ref, l_ref = o_ref[0], l_ref[0]
+            o_ref, l_ref = res[0][0], res[1][0]
         if inv_rope_theta:
             o_ref = oracle.inverse_rope(o_ref, int(wl.q_pos[t]), wl.spec.D_nope, inv_rope_theta)
-        done.append(t)
         errs.append(P.check_attention(gpu_res["o"][t], gpu_res["lse"][t], o_ref, l_ref))
-        if time.perf_counter() - t0 > seconds:
-            break
-    el = time.perf_counter() - t0
     unit = "tokens/s" if is_prefill else "queries/s"
+    cores = blas_threads or n_aff
     return dict(value=round(len(done) / el, 3), unit=unit, cores=int(cores), kind="oracle",
-                sample=f"{len(done)} of {wl.T} queries (random order, seed 0), FP64 NumPy oracle, "
-                       f"{el:.1f} s; its outputs also checked the GPU's: max|o-ref| "
-                       f"{max(e[0] for e in errs):.2e}, min per-head cos {min(e[1] for e in errs):.6f}"
+                cpu_model=model, cpu_count=n_cpu, affinity_cpus=n_aff, blas_threads=blas_threads,
+                sample=f"{len(done)} of {wl.T} queries (random order, seed 0) through the FP64 NumPy oracle "
+                       f"(indexer, top-k, attention), {el:.1f} s on {cores} threads; outside the clock its "
+                       f"outputs checked the GPU's: max|o-ref| {max(e[0] for e in errs):.2e}, min per-head cos "
+                       f"{min(e[1] for e in errs):.6f}"
                        + (f"; GPU top-k vs the oracle's (E4M3-input) top-k: mean overlap {np.mean(overlap):.4f}"
                           if overlap else ""))
 
@@ -245,7 +345,12 @@ def main():
     acc = accounting(wl, args.mxfp4)
     d0 = to_device(wl, dev)
     footprint = sum(t.numel() * t.element_size() for t in vars(d0).values() if isinstance(t, torch.Tensor))
-    copies = args.copies or int(min(256, max(2, math.ceil((1 << 30) / max(footprint, 1)))))
+    stage_keys = [k for k in ("index_scores", "topk", "decode_attn", "prefill_attn") if k in acc]
+    touched = sum(acc[k]["bytes"] for k in stage_keys)
+    # enough copies that one pass over them touches >= 1 GiB of algorithmic
+    # bytes (4x the 256 MB Infinity Cache), within 64 GiB of device memory
+    copies = args.copies or int(max(2, min(1024, math.ceil((1 << 30) / max(touched, 1)),
+                                           (64 << 30) // max(footprint, 1))))
     theta = args.inv_rope_theta
     fp4 = args.mxfp4
     opts = dict(inv_rope_theta=theta, mxfp4=fp4, fused_topk=args.fused_topk)
@@ -254,7 +359,8 @@ def main():
     stages = paths[0].stage_names
     stream = torch.cuda.current_stream()
     st = csa._stream(stream)
-    print(f"[bench] {copies} input copies of {footprint / 2**20:.1f} MiB; stages {stages}", file=sys.stderr, flush=True)
+    print(f"[bench] {copies} input copies of {footprint / 2**20:.1f} MiB ({touched / 2**20:.1f} MiB touched per "
+          f"step); stages {stages}", file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
         paths[i % copies].run(st)
@@ -298,6 +404,21 @@ def main():
         eb.record(stream)
         torch.cuda.synchronize()
         per_stage.append(ea.elapsed_time(eb) / K)
+    # Timed region 3, spread of step times: an event before every step (each
+    # interval also holds one event record's gap)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        evs[i].record(stream)
+        if graphs:
+            graphs[i % copies].replay(st)
+        else:
+            paths[i % copies].run(st)
+    evs[K].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(K)])
+    spread = dict(p10=round(float(np.percentile(step_ms, 10)), 5), median=round(float(np.median(step_ms)), 5),
+                  p90=round(float(np.percentile(step_ms, 90)), 5), how="per-step HIP events, one event gap each")
     ms_per_step = wall * 1e3 / K
     latency = None
     if graphs:
@@ -318,17 +439,28 @@ def main():
     n_items = wl.T
     value = n_items / (ms_per_step * 1e-3)
 
+    peaks = None if args.no_peaks else measured_peaks(torch, stream)
     kernels = {}
     for nm, ms in zip(stages, per_stage):
         a = acc[nm]
         kernels[nm] = dict(ms=round(ms, 5), bytes=int(a["bytes"]), flops=a["flops"],
                            GBps=round(a["bytes"] / (ms * 1e-3) / 1e9, 1),
                            TFLOPs=round(a["flops"] / (ms * 1e-3) / 1e12, 2))
+    traffic_key = name + ("_mxfp4" if fp4 else "")
     dom = max(range(len(stages)), key=lambda j: per_stage[j])
     dom_name = stages[dom]
-    roof = roofline_entry(dom_name, acc[dom_name], per_stage[dom])
+    roof = roofline_entry(dom_name, acc[dom_name], per_stage[dom], peaks)
     roof["kernel"] = dom_name
-    roof["traffic"] = measured_traffic(name + ("_mxfp4" if fp4 else ""), dom_name)
+    roof["traffic"] = measured_traffic(traffic_key, dom_name)
+    # the two kernels the metric names: the indexer scan and the attention
+    by_kernel = {}
+    for role, nm in (("indexer", "index_scores"), ("indexer", "index_topk"), ("fmha", "decode_attn"),
+                     ("fmha", "prefill_attn")):
+        if nm in kernels:
+            e = roofline_entry(nm, acc[nm], kernels[nm]["ms"], peaks)
+            e["kernel"] = nm
+            e["traffic"] = measured_traffic(traffic_key, nm)
+            by_kernel[role] = e
 
     out = dict(
         metric=PREFILL_METRIC if wl.spec.kind == "prefill" else BASE_METRIC,
@@ -340,8 +472,10 @@ def main():
                     gpu_ms_per_step=round(gpu_step, 5), launch="graph replay" if graphs else "eager calls",
                     inv_rope_theta=theta or None, indexer="MXFP4" if fp4 else "E4M3",
                     fused_topk=bool(getattr(paths[0], "fused_topk", False)),
-                    synced_step_latency=latency),
+                    synced_step_latency=latency, step_ms_spread=spread),
         roofline=roof,
+        roofline_kernels=by_kernel,
+        measured_peaks=peaks,
         kernels=kernels,
     )
     if not args.no_cpu_baseline:

@@ -347,3 +347,20 @@ def with_ring_permuted(wl: Workload, seed: int) -> Workload:
         pos[b] = wl.swa_pos[b, p]
     out.swa_nope, out.swa_rope, out.swa_pos = nope, rope, pos
     return out
+
+
+def with_fp8_scale(wl: Workload, source: str, factor: float) -> Workload:
+    """Copy of a workload whose latent ("lat") or window ("swa") nope plane is
+    stored with its per-tensor FP8 scale multiplied by `factor`: the stored
+    values (codes x scale) are re-encoded to E4M3 under the new scale with
+    torch's RNE cast (saturating), so the real values stay close while the
+    two key sources' scales differ.  Encoding only."""
+    out = dataclasses.replace(wl)
+    codes = getattr(wl, f"{source}_nope")
+    scale = float(getattr(wl, f"{source}_scale"))
+    vals = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float32) * scale
+    new_scale = scale * float(factor)
+    new = (vals / new_scale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    setattr(out, f"{source}_nope", new)
+    setattr(out, f"{source}_scale", new_scale)
+    return out

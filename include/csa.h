@@ -75,6 +75,11 @@ extern "C" {
 #define CSA_ERR_LAUNCH (-3)       /* hipPeekAtLastError() after a launch     */
 #define CSA_ERR_WORKSPACE (-4)    /* workspace missing or too small          */
 
+/* Returned by the csa_*_workspace_size queries for arguments that the
+ * matching call would reject (a shape with no kernel or an invalid size):
+ * 0 means "no workspace needed", this value means "unsupported". */
+#define CSA_WORKSPACE_UNSUPPORTED ((size_t)-1)
+
 /* Paged compressed-latent cache of one layer ([Roadmap] E1 "classical paged
  * cache": FP8 entries + BF16 rope + block table + stored scale).
  *   nope       [num_pages][page_size][D_nope] E4M3, 16-byte aligned
@@ -176,7 +181,9 @@ int csa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_idx_sc, const 
  *   scores [T][ld_scores] float, n_visible [T] int32 (values clamped to
  *   [0, ld_scores]), topk_idx [T][k] int32.
  * The workspace (bytes from csa_topk_workspace_size) may be NULL when
- * ld_scores <= 16384.  Supported: 1 <= k <= 2048.
+ * ld_scores <= 16384.  csa_topk_workspace_size returns 0 when no workspace
+ * is needed and CSA_WORKSPACE_UNSUPPORTED for arguments csa_topk rejects.
+ * Supported: 1 <= k <= 2048.
  * Errors: CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE,
  * CSA_ERR_LAUNCH. */
 size_t csa_topk_workspace_size(int32_t T, int64_t ld_scores, int32_t k);
@@ -194,7 +201,8 @@ int csa_topk(const float* scores, int64_t ld_scores, const int32_t* n_visible,
  * candidates.  Outputs: topk_idx [T][k] (ascending, -1 padding) and
  * n_visible [T].  E4M3 operands only.
  * Workspace: csa_index_topk_workspace_size(T, max_pages * page_size, k)
- * bytes (0 when a row fits one chunk; NULL is then allowed).
+ * bytes (0 when a row fits one chunk; NULL is then allowed;
+ * CSA_WORKSPACE_UNSUPPORTED for arguments csa_index_topk rejects).
  * Supported: 1 <= k <= 2048 and (max_pages * page_size) / 8192 chunks of k
  * candidates within the merge's 16384 (CSA_ERR_UNSUPPORTED otherwise).
  * Errors: CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE,
@@ -236,14 +244,21 @@ int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w,
  *   >= H*D, multiple of 8), 16-byte aligned; sink [H] float; out [.][H][D]
  *   BF16 contiguous; lse [.][H] float or NULL.
  * Precision: nope products run on FP8 MFMA (q split into two E4M3 terms
- * with a shared per-head power-of-two scale; probabilities scaled by 2^8 and
- * split into two E4M3 terms), rope products on BF16 MFMA, accumulation and
- * the softmax in FP32.
+ * with a shared per-head power-of-two scale; probabilities, at most 16
+ * relative to the running maximum of the key logits, scaled by 16 and split
+ * into two E4M3 terms), rope products on BF16 MFMA, accumulation and the
+ * softmax in FP32.  Each key source's FP8 scale (cache->nope_scale,
+ * swa->nope_scale) is applied in FP32, to the logits and to the FP32
+ * accumulators, so the two scales may differ by any ratio.  The sink joins
+ * the maximum and the denominator in FP32 after the last key, so it does
+ * not coarsen the probabilities however far it lies above the logits.
  * Workspace: needed only when the key range is split across workgroups
  * (few queries, or HCA with long context); csa_attn_workspace_size gives
- * the bytes for the preferred split, and a smaller workspace makes the
- * call use fewer splits.  CSA_ERR_WORKSPACE if even the minimum split
- * (per workgroup at most 2048 key slots) does not fit.
+ * the bytes for the preferred split (0: no split, no workspace needed;
+ * CSA_WORKSPACE_UNSUPPORTED: dims with no kernel, or more key slots than
+ * 128 splits of 2048 hold), and a smaller workspace makes the call use
+ * fewer splits.  CSA_ERR_WORKSPACE if even the minimum split (per
+ * workgroup at most 2048 key slots) does not fit.
  * Supported: H >= 1, (D_nope, D_rope) in {(448,64), (48,16)},
  * 1 <= W <= 1024, 0 <= k <= 2048. */
 size_t csa_attn_workspace_size(int32_t n_queries, int32_t H, int32_t D_nope,

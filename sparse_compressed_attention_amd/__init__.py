@@ -27,6 +27,7 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 CSA_OK = 0
+CSA_WORKSPACE_UNSUPPORTED = (1 << (8 * ctypes.sizeof(ctypes.c_size_t))) - 1
 
 
 class CsaError(RuntimeError):
@@ -153,6 +154,64 @@ def _check(fn: str, rc: int):
         raise CsaError(fn, rc)
 
 
+def _shape(t, name: str, want: tuple):
+    """Exact shape check; None entries of `want` match any size."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        raise ValueError(f"{name} has shape {got}, expected {tuple('*' if w is None else w for w in want)}")
+
+
+def _rows_at_least(t, name: str, n: int):
+    if t.dim() < 1 or t.shape[0] < n:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, needs at least {n} rows")
+
+
+def _attn_shapes(q, cache, topk_idx, k, q_pos, sink, out, lse):
+    """Shapes shared by both attention calls: q [n][H][D] (D = the cache's
+    D_nope + D_rope), out [n][H][D], lse [n][H], topk_idx [n][k], q_pos [n],
+    sink with at least H entries.  Returns (n, H)."""
+    if q.dim() != 3:
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected [queries][H][D]")
+    n, H, D = q.shape
+    dn, dr = cache.nope.shape[-1], cache.rope.shape[-1]
+    if D != dn + dr:
+        raise ValueError(f"q has {D} dims per head; the cache holds {dn} + {dr}")
+    _shape(out, "out", (n, H, D))
+    if lse is not None:
+        _shape(lse, "lse", (n, H))
+    if topk_idx is not None:
+        _shape(topk_idx, "topk_idx", (n, int(k)))
+    _shape(q_pos, "q_pos", (n,))
+    if sink.dim() != 1 or sink.shape[0] < H:
+        raise ValueError(f"sink has shape {tuple(sink.shape)}, needs one entry per head ({H})")
+    return n, H
+
+
+def _decode_shapes(q, cache, topk_idx, k, swa, q_pos, sink, out, lse):
+    """Decode: the ring and the page table hold at least one row per query,
+    with the cache's dims."""
+    B, _ = _attn_shapes(q, cache, topk_idx, k, q_pos, sink, out, lse)
+    _rows_at_least(cache.page_table, "cache.page_table", B)
+    if swa.nope.dim() != 3:
+        raise ValueError(f"swa.nope has shape {tuple(swa.nope.shape)}, expected [B][W][D_nope]")
+    nb, W, dn = swa.nope.shape
+    if nb < B or dn != cache.nope.shape[-1]:
+        raise ValueError(f"swa.nope has shape {tuple(swa.nope.shape)}, expected [>= {B}][W][{cache.nope.shape[-1]}]")
+    _shape(swa.rope, "swa.rope", (nb, W, cache.rope.shape[-1]))
+    _shape(swa.pos, "swa.pos", (nb, W))
+
+
+def _prefill_shapes(q, cache, seq, topk_idx, k, swa_nope, swa_rope, q_pos, sink, out, lse):
+    """Prefill: the linear window buffer has as many rope rows as nope rows,
+    with the cache's dims; `seq` is a row of the page table."""
+    _attn_shapes(q, cache, topk_idx, k, q_pos, sink, out, lse)
+    if not 0 <= int(seq) < cache.page_table.shape[0]:
+        raise ValueError(f"seq {seq} is not a row of the page table ({cache.page_table.shape[0]} rows)")
+    if swa_nope.dim() != 2 or swa_nope.shape[1] != cache.nope.shape[-1]:
+        raise ValueError(f"swa_nope has shape {tuple(swa_nope.shape)}, expected [L][{cache.nope.shape[-1]}]")
+    _shape(swa_rope, "swa_rope", (swa_nope.shape[0], cache.rope.shape[-1]))
+
+
 @dataclass
 class LatentCache:
     """Paged compressed-latent cache of one layer (see csa_latent_cache)."""
@@ -170,7 +229,8 @@ class LatentCache:
         _need(self.n_comp, "cache.n_comp", _I32, 1)
         P, ps, dn = self.nope.shape
         if tuple(self.rope.shape[:2]) != (P, ps):
-            raise ValueError("cache.rope must be [P][page_size][D_rope] like cache.nope")
+            raise ValueError(f"cache.rope has shape {tuple(self.rope.shape)}, expected [{P}][{ps}][D_rope] "
+                             "like cache.nope")
         if self.n_comp.shape[0] != self.page_table.shape[0]:
             raise ValueError("cache.n_comp must have one entry per page-table row")
         return _LatentCacheC(self.nope.data_ptr(), self.rope.data_ptr(), float(self.nope_scale),
@@ -251,8 +311,15 @@ def csa_index_scores_mxfp4(q_idx, q_idx_sc, w, k_idx, k_idx_sc, page_table, n_co
     _check("csa_index_scores_mxfp4", rc)
 
 
+def _ws_bytes(fn: str, n: int) -> int:
+    if n == CSA_WORKSPACE_UNSUPPORTED:
+        raise ValueError(f"{fn}: unsupported arguments (the matching call would reject them)")
+    return int(n)
+
+
 def csa_index_topk_workspace_size(T: int, max_entries: int, k: int) -> int:
-    return int(load_library().csa_index_topk_workspace_size(int(T), int(max_entries), int(k)))
+    return _ws_bytes("csa_index_topk_workspace_size",
+                     load_library().csa_index_topk_workspace_size(int(T), int(max_entries), int(k)))
 
 
 def csa_index_topk(q_idx, q_idx_scale, w, k_idx, k_idx_scale, page_table, n_comp, q_pos, q_seq, ratio_m, k,
@@ -281,7 +348,7 @@ def csa_index_topk(q_idx, q_idx_scale, w, k_idx, k_idx_scale, page_table, n_comp
 
 
 def csa_topk_workspace_size(T: int, ld_scores: int, k: int) -> int:
-    return int(load_library().csa_topk_workspace_size(int(T), int(ld_scores), int(k)))
+    return _ws_bytes("csa_topk_workspace_size", load_library().csa_topk_workspace_size(int(T), int(ld_scores), int(k)))
 
 
 def csa_topk(scores, n_visible, k, topk_idx, workspace=None, stream=None):
@@ -300,12 +367,14 @@ def csa_topk(scores, n_visible, k, topk_idx, workspace=None, stream=None):
 
 
 def csa_attn_workspace_size(n_queries: int, H: int, D_nope: int, D_rope: int, max_keys_per_query: int) -> int:
-    return int(load_library().csa_attn_workspace_size(int(n_queries), int(H), int(D_nope), int(D_rope),
-                                                      int(max_keys_per_query)))
+    return _ws_bytes("csa_attn_workspace_size",
+                     load_library().csa_attn_workspace_size(int(n_queries), int(H), int(D_nope), int(D_rope),
+                                                            int(max_keys_per_query)))
 
 
 def csa_decode_attn(q, cache: LatentCache, topk_idx, k, swa: SwaRing, q_pos, sink, softmax_scale, out,
                     lse=None, workspace=None, stream=None, inv_rope_theta=0.0):
+    _decode_shapes(q, cache, topk_idx, k, swa, q_pos, sink, out, lse)
     _need(q, "q", _B16, 3, contiguous=False)
     _need(q_pos, "q_pos", _I32, 1)
     _need(sink, "sink", _F32, 1)
@@ -328,6 +397,7 @@ def csa_decode_attn(q, cache: LatentCache, topk_idx, k, swa: SwaRing, q_pos, sin
 
 def csa_prefill_attn(q, cache: LatentCache, seq, topk_idx, k, swa_nope, swa_rope, swa_scale, swa_first_pos, W,
                      q_pos, sink, softmax_scale, out, lse=None, workspace=None, stream=None, inv_rope_theta=0.0):
+    _prefill_shapes(q, cache, seq, topk_idx, k, swa_nope, swa_rope, q_pos, sink, out, lse)
     _need(q, "q", _B16, 3, contiguous=False)
     _need(q_pos, "q_pos", _I32, 1)
     _need(sink, "sink", _F32, 1)
@@ -464,6 +534,9 @@ class DecodePath(_Path):
                 plan.append(self._index_stage())
                 plan.append(("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), B, self.k, _ptr(self.topk),
                                           _ptr(self.topk_ws), tw)))
+        _decode_shapes(self.q, self.cache, self.topk, self.k, self.swa, self.q_pos, self.sink, self.out, self.lse)
+        _need(self.q_pos, "q_pos", _I32, 1)
+        _need(self.sink, "sink", _F32, 1)
         aw = 0 if self.attn_ws is None else self.attn_ws.numel()
         plan.append(("csa_decode_attn", (
             _ptr(self.q), self.q.stride(0), ctypes.byref(self._cc), _ptr(self.topk), self.k, ctypes.byref(self._sc),
@@ -507,6 +580,10 @@ class PrefillPath(_Path):
 
     def _plan(self):
         T, H, _ = self.q.shape
+        _prefill_shapes(self.q, self.cache, self.seq, self.topk, self.k, self.swa_nope, self.swa_rope, self.q_pos,
+                        self.sink, self.out, self.lse)
+        _need(self.q_pos, "q_pos", _I32, 1)
+        _need(self.sink, "sink", _F32, 1)
         self._cc = self.cache.as_c()
         _need(self.q_idx, "q_idx", _U8, 3)
         _need(self.k_idx, "k_idx", _U8, 3)

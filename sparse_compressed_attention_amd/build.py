@@ -59,11 +59,24 @@ def build_c_driver(verbose: bool = False) -> str:
     return C_DRIVER
 
 
-def build(verbose: bool = False) -> str:
-    fd, tmp = tempfile.mkstemp(prefix=".libcsa.", suffix=".so.tmp", dir=PKG_DIR)
+PEAK_LIB_PATH = os.path.join(PKG_DIR, "libcsa_peak.so")
+
+
+def peak_build_command(out_path: str) -> list[str]:
+    """The benchmark's peak probes (plain copy, FP8 MFMA loop): a library of
+    their own, never loaded by the CSA path."""
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        os.path.join(CSRC, "peak.hip"), "-o", out_path,
+    ]
+
+
+def _build_lib(make_cmd, dest: str, verbose: bool) -> None:
+    fd, tmp = tempfile.mkstemp(prefix="." + os.path.basename(dest) + ".", suffix=".so.tmp", dir=PKG_DIR)
     os.close(fd)
     try:
-        cmd = build_command(tmp)
+        cmd = make_cmd(tmp)
         res = subprocess.run(cmd, capture_output=True, text=True)
         msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                          if "packed-fp32-ops" not in l)
@@ -71,10 +84,15 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + msgs)
         if verbose and msgs.strip():
             print(msgs, file=sys.stderr)
-        os.replace(tmp, LIB_PATH)
+        os.replace(tmp, dest)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+
+
+def build(verbose: bool = False) -> str:
+    _build_lib(build_command, LIB_PATH, verbose)
+    _build_lib(peak_build_command, PEAK_LIB_PATH, verbose)
     build_c_driver(verbose)
     return LIB_PATH
 

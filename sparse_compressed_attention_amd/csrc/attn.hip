@@ -46,10 +46,14 @@
 //  * online softmax in FP32, exp2 domain; each lane owns one head.  The
 //    running max is raised lazily: only when a tile's max exceeds it by more
 //    than 2^tau (tau = 4), so probabilities stay <= 2^tau and the O rescale
-//    runs on few tiles.  The sink starts the running max and denominator;
+//    runs on few tiles.  The sink joins the max and the denominator in FP32
+//    after the last tile, so P is always quantised relative to the largest
+//    key logit, however large the sink;
 //  * PV: O^T (dims x heads) += X^T . P^T on v_mfma 16x16x128 FP8 with
-//    K = [64 keys, P hi | 64 keys, P lo] (P x key-scale ratio x 2^(8 - tau)
-//    as two E4M3 terms); X^T comes from the same LDS tile through
+//    K = [64 keys, P hi | 64 keys, P lo] (P x 2^(8 - tau) as two E4M3 terms,
+//    the keys' E4M3 codes unscaled; the key source's FP8 scale is applied in
+//    FP32, with one rescale of the accumulators where the key range passes
+//    from compressed entries to window rows); X^T comes from the same LDS tile through
 //    ds_read_b64_tr_b8 (two reads per 16 dims, used for both terms).  Rope
 //    dims use ds_read_b64_tr_b16 and v_mfma 16x16x32 BF16 with P in BF16.
 //    P never leaves registers.
@@ -374,12 +378,19 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   }
   const float cql = cq * p.lat_scale, cqs = cq * p.swa_scale;
 
-  // ---- softmax state (exp2 domain), identical in both dim halves
+  // ---- softmax state (exp2 domain), identical in every dim part.  The sink
+  // stays out of the running max: the probabilities are quantised relative to
+  // the largest key logit, and the sink joins the max and the denominator in
+  // FP32 at the end (split 0 only).
   const bool sink_here = bk.split == 0 && head_ok;
   const float sink2 = head_ok ? sink_raw * kLog2e : -__builtin_inff();
-  float m_run = sink_here ? sink2 : -__builtin_inff();
-  // (with split P the sink's share of the denominator is counted by part 0)
-  float l_run = (sink_here && g == 0 && sink2 > -__builtin_inff() && DP == 0) ? 1.0f : 0.0f;
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+  // The FP8 accumulator holds p x (E4M3 code) in the unit of one key source's
+  // scale: the compressed entries' until the first window tile, whose arrival
+  // rescales the nope accumulators by lat_scale / swa_scale (tiles never mix
+  // the two sources, and the window tiles come last).
+  bool o_swa = kv0 >= sel_end;
   v4f O[HF::NO];
 #pragma unroll
   for (int i = 0; i < HF::NO; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -543,7 +554,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         for (int i = 0; i < HF::NO; ++i) O[i] *= alpha;
       }
     }
-    const float kq = tile_swa ? p.pscale_swa : p.pscale_lat;
+    const float kq = p.pscale;
     float psum = 0.0f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -554,8 +565,8 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         pr[i] = __builtin_amdgcn_exp2f(tot[st][i] - delta);   // exp2(-inf) = 0 for masked keys
         psum += pr[i];
       }
-      // nope operand bytes: hi of p x key-scale ratio x 2^(8 - tau), lo = the
-      // rounding residual; rope operand: p in BF16
+      // nope operand bytes: hi of p x 2^(8 - tau), lo = the rounding
+      // residual; rope operand: p in BF16
       const float x0 = pr[0] * kq, x1 = pr[1] * kq, x2 = pr[2] * kq, x3 = pr[3] * kq;
       const int w = pack4_fp8(x0, x1, x2, x3);
       const v2f b01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
@@ -716,6 +727,13 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
         }
       }
     }
+    if (tile_swa && !o_swa) {
+      // first window tile: the nope accumulators change unit (uniform branch,
+      // taken at most once)
+#pragma unroll
+      for (int i = 0; i < HF::NPT; ++i) O[i] *= p.lat_over_swa;
+      o_swa = true;
+    }
     __builtin_amdgcn_sched_barrier(0);
     pv(xb, pq);
     if (refill) issue_quads(nbuf, 2);
@@ -734,8 +752,20 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   }
   if (!tile_ok) return;
 
+  // ---- the sink joins the max and the denominator (split 0): M = max(m, sink),
+  // O and L rescaled by 2^(m - M), plus 2^(sink - M) in L
+  float M = m_run, oscale = 1.0f;
+  if (sink_here) {
+    const float Ms = fmaxf(m_run, sink2);
+    if (Ms > -__builtin_inff()) {
+      oscale = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - Ms);
+      L = L * oscale + __builtin_amdgcn_exp2f(sink2 - Ms);
+      M = Ms;
+    }
+  }
+  const float nope_unit = (o_swa ? p.swa_scale : p.lat_scale) * p.inv_pscale * oscale;
+
   // ---- output of this part's dims (the softmax state is the same in every part)
-  const float M = m_run;
   const bool final_out = p.n_splits == 1;
   const float invL = (final_out && L > 0.0f) ? 1.0f / L : 0.0f;
   // inverse RoPE of the rope dims at the query position, when this
@@ -762,7 +792,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 #pragma unroll
     for (int j = 0; j < HF::NO; ++j) {
       const bool nope = j < HF::NPT;
-      const float unit = nope ? p.nope_unit : 1.0f;
+      const float unit = nope ? nope_unit : oscale;
       const int dim = nope ? 16 * (HF::PT0 + j) + 4 * g : DN + 16 * (j - HF::NPT) + 4 * g;
       v4f v = O[j] * unit;
       if constexpr (HF::NRT > 0) {

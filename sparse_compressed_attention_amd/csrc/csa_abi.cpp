@@ -214,9 +214,9 @@ int csa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_idx_sc, const 
 }
 
 size_t csa_index_topk_workspace_size(int32_t T, int64_t max_entries, int32_t k) {
-  if (T < 1 || max_entries < 1 || k < 1 || k > kTopkMaxK) return 0;
+  if (T < 1 || max_entries < 1 || k < 1 || k > kTopkMaxK) return CSA_WORKSPACE_UNSUPPORTED;
   const TopkPlan pl = plan_index_topk(T, max_entries, k);
-  return pl.ok ? pl.ws_bytes : 0;
+  return pl.ok ? pl.ws_bytes : CSA_WORKSPACE_UNSUPPORTED;
 }
 
 int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w, const uint8_t* k_idx, float k_idx_scale,
@@ -273,9 +273,9 @@ int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w, cons
 }
 
 size_t csa_topk_workspace_size(int32_t T, int64_t ld_scores, int32_t k) {
-  if (T < 1 || ld_scores < 1 || k < 1 || k > kTopkMaxK) return 0;
+  if (T < 1 || ld_scores < 1 || k < 1 || k > kTopkMaxK) return CSA_WORKSPACE_UNSUPPORTED;
   const TopkPlan pl = plan_topk(T, ld_scores, k);
-  return pl.ok ? pl.ws_bytes : 0;
+  return pl.ok ? pl.ws_bytes : CSA_WORKSPACE_UNSUPPORTED;
 }
 
 int csa_topk(const float* scores, int64_t ld_scores, const int32_t* n_visible, int32_t T, int32_t k,
@@ -307,9 +307,10 @@ int csa_topk(const float* scores, int64_t ld_scores, const int32_t* n_visible, i
 
 size_t csa_attn_workspace_size(int32_t n_queries, int32_t H, int32_t D_nope, int32_t D_rope,
                                int32_t max_keys_per_query) {
-  if (n_queries < 1 || H < 1 || !dims_supported(D_nope, D_rope) || max_keys_per_query < 0) return 0;
+  if (n_queries < 1 || H < 1 || !dims_supported(D_nope, D_rope) || max_keys_per_query < 0)
+    return CSA_WORKSPACE_UNSUPPORTED;
   AttnPlan pl;
-  if (!plan_attn(n_queries, H, D_nope + D_rope, max_keys_per_query, 0, false, &pl)) return 0;
+  if (!plan_attn(n_queries, H, D_nope + D_rope, max_keys_per_query, 0, false, &pl)) return CSA_WORKSPACE_UNSUPPORTED;
   return pl.ws_bytes;
 }
 
@@ -321,12 +322,10 @@ static void set_inv_rope(AttnParams& p, float theta) {
 }
 
 static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t workspace_bytes, void* stream) {
-  const float smax = std::max(p.lat_scale, p.swa_scale);
-  const float pmul = std::ldexp(1.0f, 8 - kAttnTau);
   p.sm_log2 = p.sm_scale * 1.4426950408889634f;
-  p.pscale_lat = p.lat_scale / smax * pmul;
-  p.pscale_swa = p.swa_scale / smax * pmul;
-  p.nope_unit = smax / pmul;
+  p.pscale = std::ldexp(1.0f, 8 - kAttnTau);
+  p.inv_pscale = std::ldexp(1.0f, kAttnTau - 8);
+  p.lat_over_swa = p.lat_scale / p.swa_scale;
   // division by the page size as a multiply-shift: with l = ceil(log2 d),
   // M = ceil(2^(32 + l) / d) has M d - 2^(32 + l) < d <= 2^l, so
   // floor(n M / 2^(32 + l)) == floor(n / d) for every n < 2^31

@@ -69,9 +69,9 @@ struct AttnParams {
   float lat_scale, swa_scale;
   float sm_scale;          // softmax scale (natural-log units)
   // derived on the host (uniform): sm_scale*log2(e); FP8 probability scale
-  // per key source (key scale / max scale * 2^(8 - tau)); value unit of the
-  // FP8 accumulator (max scale / 2^(8 - tau))
-  float sm_log2, pscale_lat, pscale_swa, nope_unit;
+  // 2^(8 - tau) and its inverse; lat_scale / swa_scale (the rescale of the
+  // FP8 accumulators where the key range passes to the window rows)
+  float sm_log2, pscale, inv_pscale, lat_over_swa;
   // inverse RoPE of the output's rope dims at the query position (inv_rope
   // != 0) with base 2^rope_log2_theta
   double rope_log2_theta;

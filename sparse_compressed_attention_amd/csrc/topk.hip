@@ -36,7 +36,7 @@ namespace {
 
 using namespace topk_sel;
 
-// (at most 64 VGPRs, so that four 512-thread workgroups share a CU)
+// (launch bounds: six 512-thread workgroups per CU when registers allow)
 template <int BLOCK, int SEG>
 __global__ __launch_bounds__(BLOCK, 6) void topk_chunk_kernel(TopkParams p) {
   __shared__ TopkShared<BLOCK> sh;

@@ -97,6 +97,10 @@ int main(int argc, char** argv) {
   auto* lse = static_cast<float*>(device_buffer((size_t)B * H * 4));
   const size_t tws = csa_topk_workspace_size(B, ld, k);
   const size_t aws = csa_attn_workspace_size(B, H, Dn, Dr, k + W);
+  if (tws == CSA_WORKSPACE_UNSUPPORTED || aws == CSA_WORKSPACE_UNSUPPORTED) {
+    fprintf(stderr, "workspace query: unsupported shape\n");
+    return 2;
+  }
   void* topk_ws = tws ? device_buffer(tws) : nullptr;
   void* attn_ws = aws ? device_buffer(aws) : nullptr;
 

@@ -58,8 +58,14 @@ def test_workspace_sizes(lib):
     assert csa.csa_topk_workspace_size(4, 131072, 512) == 4 * 16 * 512 * 8
     # 32 candidates per chunk: up to 512 chunks of 8192 fit the merge
     assert csa.csa_topk_workspace_size(2, 512 * 8192, 32) == 2 * 512 * 32 * 8
-    # rows too long for two levels of 16384 candidates
-    assert csa.csa_topk_workspace_size(1, 1 << 22, 2048) == 0
+    # rows too long for two levels of 16384 candidates: "unsupported", told
+    # apart from "no workspace needed" (0)
+    assert lib.csa_topk_workspace_size(1, 1 << 22, 2048) == csa.CSA_WORKSPACE_UNSUPPORTED
+    with pytest.raises(ValueError, match="unsupported"):
+        csa.csa_topk_workspace_size(1, 1 << 22, 2048)
+    assert lib.csa_topk_workspace_size(4, 8192, 4096) == csa.CSA_WORKSPACE_UNSUPPORTED   # k > 2048
+    assert lib.csa_index_topk_workspace_size(64, 8192, 0) == csa.CSA_WORKSPACE_UNSUPPORTED
+    assert csa.csa_index_topk_workspace_size(64, 2048, 512) == 0
     # many queries: one workgroup per (query, 32 heads), no split
     assert csa.csa_attn_workspace_size(64, 128, 448, 64, 640) == 0
     # one query: split over workgroups, partials of 512 + 2 floats per head
@@ -67,8 +73,10 @@ def test_workspace_sizes(lib):
     ws = csa.csa_attn_workspace_size(1, 128, 448, 64, 640)
     assert ws > 0 and ws % (128 * 516 * 4) == 0
     # key ranges beyond 128 splits of 2048 slots are not supported
-    assert csa.csa_attn_workspace_size(1, 128, 448, 64, 128 * 2048) == 0
-    assert csa.csa_attn_workspace_size(1, 128, 100, 64, 640) == 0   # unsupported dims
+    assert lib.csa_attn_workspace_size(1, 128, 448, 64, 128 * 2048) == csa.CSA_WORKSPACE_UNSUPPORTED
+    assert lib.csa_attn_workspace_size(1, 128, 100, 64, 640) == csa.CSA_WORKSPACE_UNSUPPORTED   # unsupported dims
+    with pytest.raises(ValueError, match="unsupported"):
+        csa.csa_attn_workspace_size(1, 128, 100, 64, 640)
 
 
 def test_null_arguments_rejected_without_launch(lib):
@@ -166,3 +174,78 @@ def test_attention_without_enough_workspace_is_rejected_before_launch(lib):
     rc = lib.csa_decode_attn(fake, 512 * 128, ctypes.byref(cache), None, 0, ctypes.byref(ring), fake, fake,
                              1.0, 0.0, 2, 128, fake, None, fake, 1024, None)
     assert rc == -4      # far too small
+
+
+# ---------------------------------------------------------------- binding shape checks
+def _decode_args(B=2, H=8, dn=48, dr=16, W=32, k=16):
+    import torch
+    D = dn + dr
+    cache = csa.LatentCache(torch.zeros(4, 64, dn, dtype=torch.uint8), torch.zeros(4, 64, dr, dtype=torch.bfloat16),
+                            1.0, torch.zeros(B, 2, dtype=torch.int32), torch.zeros(B, dtype=torch.int32), 4)
+    swa = csa.SwaRing(torch.zeros(B, W, dn, dtype=torch.uint8), torch.zeros(B, W, dr, dtype=torch.bfloat16), 1.0,
+                      torch.zeros(B, W, dtype=torch.int32))
+    return dict(q=torch.zeros(B, H, D, dtype=torch.bfloat16), cache=cache, topk_idx=torch.zeros(B, k, dtype=torch.int32),
+                k=k, swa=swa, q_pos=torch.zeros(B, dtype=torch.int32), sink=torch.zeros(H), softmax_scale=0.125,
+                out=torch.zeros(B, H, D, dtype=torch.bfloat16), lse=torch.zeros(B, H))
+
+
+@pytest.mark.parametrize("change,match", [
+    (lambda a, t: a.update(out=t.zeros(2, 8, 63, dtype=t.bfloat16)), "out has shape"),
+    (lambda a, t: a.update(out=t.zeros(3, 8, 64, dtype=t.bfloat16)), "out has shape"),
+    (lambda a, t: a.update(lse=t.zeros(2, 7)), "lse has shape"),
+    (lambda a, t: a.update(topk_idx=t.zeros(2, 15, dtype=t.int32)), "topk_idx has shape"),
+    (lambda a, t: a.update(topk_idx=t.zeros(1, 16, dtype=t.int32)), "topk_idx has shape"),
+    (lambda a, t: a.update(q_pos=t.zeros(3, dtype=t.int32)), "q_pos has shape"),
+    (lambda a, t: a.update(sink=t.zeros(7)), "sink has shape"),
+    (lambda a, t: a.update(q=t.zeros(2, 8, 60, dtype=t.bfloat16)), "dims per head"),
+    (lambda a, t: a["swa"].__setattr__("nope", t.zeros(1, 32, 48, dtype=t.uint8)), "swa.nope has shape"),
+    (lambda a, t: a["swa"].__setattr__("nope", t.zeros(2, 32, 40, dtype=t.uint8)), "swa.nope has shape"),
+    (lambda a, t: a["swa"].__setattr__("rope", t.zeros(2, 32, 8, dtype=t.bfloat16)), "swa.rope has shape"),
+    (lambda a, t: a["swa"].__setattr__("rope", t.zeros(2, 31, 16, dtype=t.bfloat16)), "swa.rope has shape"),
+    (lambda a, t: a["swa"].__setattr__("pos", t.zeros(2, 16, dtype=t.int32)), "swa.pos has shape"),
+    (lambda a, t: a["cache"].__setattr__("page_table", t.zeros(1, 2, dtype=t.int32)), "cache.page_table"),
+])
+def test_decode_binding_rejects_mismatched_shapes(change, match):
+    import torch
+    a = _decode_args()
+    change(a, torch)
+    with pytest.raises(ValueError, match=match):
+        csa.csa_decode_attn(**a)
+
+
+def test_decode_binding_shape_check_passes_consistent_shapes():
+    # consistent shapes get past the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU tensor"):
+        csa.csa_decode_attn(**_decode_args())
+
+
+def _prefill_args(T=5, H=8, dn=48, dr=16, L=40, k=16):
+    import torch
+    a = _decode_args(B=1, H=H, dn=dn, dr=dr, k=k)
+    D = dn + dr
+    return dict(q=torch.zeros(T, H, D, dtype=torch.bfloat16), cache=a["cache"], seq=0,
+                topk_idx=torch.zeros(T, k, dtype=torch.int32), k=k, swa_nope=torch.zeros(L, dn, dtype=torch.uint8),
+                swa_rope=torch.zeros(L, dr, dtype=torch.bfloat16), swa_scale=1.0, swa_first_pos=0, W=32,
+                q_pos=torch.zeros(T, dtype=torch.int32), sink=torch.zeros(H), softmax_scale=0.125,
+                out=torch.zeros(T, H, D, dtype=torch.bfloat16), lse=torch.zeros(T, H))
+
+
+@pytest.mark.parametrize("change,match", [
+    (lambda a, t: a.update(swa_rope=t.zeros(39, 16, dtype=t.bfloat16)), "swa_rope has shape"),
+    (lambda a, t: a.update(swa_nope=t.zeros(40, 32, dtype=t.uint8)), "swa_nope has shape"),
+    (lambda a, t: a.update(seq=1), "page table"),
+    (lambda a, t: a.update(topk_idx=t.zeros(4, 16, dtype=t.int32)), "topk_idx has shape"),
+    (lambda a, t: a.update(lse=t.zeros(5, 8, 1)), "lse has shape"),
+    (lambda a, t: a.update(q_pos=t.zeros(6, dtype=t.int32)), "q_pos has shape"),
+])
+def test_prefill_binding_rejects_mismatched_shapes(change, match):
+    import torch
+    a = _prefill_args()
+    change(a, torch)
+    with pytest.raises(ValueError, match=match):
+        csa.csa_prefill_attn(**a)
+
+
+def test_prefill_binding_shape_check_passes_consistent_shapes():
+    with pytest.raises(ValueError, match="GPU tensor"):
+        csa.csa_prefill_attn(**_prefill_args())

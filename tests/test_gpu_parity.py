@@ -7,6 +7,7 @@ HCA mode, prefill, and every full-size configuration in the launch shape the
 benchmark times, checked on sampled queries.
 """
 import dataclasses
+import math
 import sys
 
 import numpy as np
@@ -286,8 +287,8 @@ def test_fused_index_topk_equals_two_calls(case):
     fused = make_path(d, fused_topk=True)
     assert fused.stage_names == ("index_topk", "decode_attn")
     two.run()
-    # three calls in a row on one (zero-filled) workspace: the arrival
-    # counters of long rows must be back at zero after every call
+    # three calls in a row on one workspace: every call leaves the same
+    # indices (nothing carries over from the previous call's candidates)
     for rep in range(3):
         fused.topk.fill_(-7)
         fused.run()
@@ -527,7 +528,7 @@ def test_topk_kernel_exact_on_synthetic_rows(k):
         else:
             v = rng.standard_normal(n).astype(np.float32)
             v[rng.random(n) < 0.3] = -np.inf
-        row = np.full(ld, np.nan, dtype=np.float32)   # columns past n_visible must never be read
+        row = np.full(ld, np.nan, dtype=np.float32)   # columns past n_visible may be loaded but must never count
         row[:n] = v
         rows.append(row)
         nvis.append(n)
@@ -584,3 +585,83 @@ def test_indexer_page_sizes(page_size):
     say(f"case indexer page {page_size}")
     spec = ci.small_spec(ctx_lens=[4000, 1508, 2900], shuffle_pages=True, page_size=page_size)
     check_full(ci.generate(spec, seed=200 + page_size))
+
+
+# --------------------------------------------------------------- precision: sinks and FP8 scales
+def _precision_case(case, seed):
+    """Workloads that reach each attention launch shape: few queries (key
+    range split over workgroups, then the merge), 64 decode queries (one
+    workgroup per 32 heads, four dim parts, no split), and a 160-query
+    prefill chunk (64-head workgroups, two dim parts, no split)."""
+    if case == "decode_merge":
+        return ci.generate(ci.small_spec(ctx_lens=[2400, 900, 1500], shuffle_pages=True), seed=seed), None
+    if case == "decode_wide":
+        rng = np.random.default_rng(seed)
+        lens = [int(x) * 4 for x in rng.integers(150, 700, size=64)]
+        spec = ci.small_spec(name="wide64", ctx_lens=lens, shuffle_pages=True)
+        return ci.generate(spec, seed=seed), [0, 1, 17, 40, 63]
+    spec = ci.Spec(name="prefill_160", kind="prefill", ctx_lens=[5000], T_prefill=160)
+    return ci.generate(spec, seed=seed), [0, 1, 63, 64, 159]
+
+
+@pytest.mark.parametrize("sink", [8.0, 10.0, 12.0])
+@pytest.mark.parametrize("case", ["decode_merge", "decode_wide", "prefill"])
+def test_sink_far_above_the_logits(case, sink):
+    # logits are about N(0, 1) here; a sink of 8..12 dominates the softmax.
+    # The probabilities must still be quantised relative to the largest key
+    # logit, so the (small) output keeps its direction.  Even heads get the
+    # large sink, odd heads keep their N(0, 1) draw.
+    say(f"case sink {sink} ({case})")
+    wl, qs = _precision_case(case, seed=300 + int(sink))
+    sk = wl.sink.copy()
+    sk[0::2] = sink
+    check_full(dataclasses.replace(wl, sink=sk), queries=qs)
+
+
+@pytest.mark.parametrize("ratio_log2", [-8, -4, 4, 8])
+@pytest.mark.parametrize("case", ["decode_merge", "decode_wide", "prefill"])
+def test_unequal_latent_and_window_fp8_scales(case, ratio_log2):
+    # latent scale / window scale = 2^ratio_log2: the larger scale is raised
+    # and its plane re-encoded, so both sources keep N(0, 1)-sized values
+    # (the one with the raised scale on a coarser grid)
+    say(f"case FP8 scales latent/window = 2^{ratio_log2} ({case})")
+    wl, qs = _precision_case(case, seed=320 + ratio_log2)
+    if ratio_log2 > 0:
+        wl = ci.with_fp8_scale(wl, "lat", 2.0 ** ratio_log2)
+    else:
+        wl = ci.with_fp8_scale(wl, "swa", 2.0 ** -ratio_log2)
+    assert math.isclose(wl.lat_scale / wl.swa_scale, 2.0 ** ratio_log2, rel_tol=0.5)
+    check_full(wl, queries=qs)
+
+
+def test_topk_all_equals_hca_mode():
+    # every row has at most k visible entries, so the top-k list holds every
+    # visible entry: csa_decode_attn on that list and in HCA mode (no list)
+    # attend the same keys
+    say("case top-k = all vs HCA mode")
+    spec = ci.small_spec(name="all_vs_hca", ctx_lens=[1500, 900, 2047, 2048], shuffle_pages=True)
+    wl = ci.generate(spec, seed=331)
+    s = wl.spec
+    d = to_device(wl, "cuda")
+    path = make_path(d)
+    out_k, lse_k = path.run()
+    nv = path.n_vis.cpu().numpy()
+    assert (nv <= s.k).all()
+    cache = csa.LatentCache(d.lat_nope, d.lat_rope, d.lat_scale, d.page_table, d.n_comp, s.m)
+    swa = csa.SwaRing(d.swa_nope, d.swa_rope, d.swa_scale, d.swa_pos)
+    max_keys = d.page_table.shape[1] * d.lat_nope.shape[1] + s.W
+    ws_bytes = csa.csa_attn_workspace_size(wl.T, s.H, s.D_nope, s.D_rope, max_keys)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device="cuda")
+    out_h = torch.empty_like(out_k)
+    lse_h = torch.empty_like(lse_k)
+    csa.csa_decode_attn(d.q, cache, None, 0, swa, d.q_pos, d.sink, s.sigma, out_h, lse_h, workspace=ws)
+    torch.cuda.synchronize()
+    topk = path.topk.cpu().numpy()
+    ok, oh = P.bf16_to_f64(out_k), P.bf16_to_f64(out_h)
+    lk, lh = lse_k.cpu().numpy().astype(np.float64), lse_h.cpu().numpy().astype(np.float64)
+    for t in range(wl.T):
+        assert sorted(topk[t][topk[t] >= 0].tolist()) == list(range(int(nv[t])))
+        err, cos = P.check_attention(ok[t], lk[t], oh[t], lh[t])
+        o_ref, l_ref = P.reference_attention_on(wl, t, None)
+        P.check_attention(oh[t], lh[t], o_ref, l_ref)
+        say(f"  query {t}: {int(nv[t])} visible, top-k vs HCA max|diff| {err:.2e}, min cos {cos:.6f}")
