@@ -74,6 +74,7 @@ extern "C" {
 #define CSA_ERR_UNSUPPORTED (-2)  /* a shape no kernel is built for         */
 #define CSA_ERR_LAUNCH (-3)       /* hipPeekAtLastError() after a launch     */
 #define CSA_ERR_WORKSPACE (-4)    /* workspace missing or too small          */
+#define CSA_ERR_TOO_LARGE (-5)    /* beyond the fixed scratch of a _noalloc call */
 
 /* Returned by the csa_*_workspace_size queries for arguments that the
  * matching call would reject (a shape with no kernel or an invalid size):
@@ -275,6 +276,29 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride,
                     float inv_rope_theta, int32_t B, int32_t H,
                     uint16_t* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, result and errors as csa_decode_attn,
+ * minus the workspace: the partial results of split key ranges go to a
+ * static device array inside the library, one per GPU, of
+ * CSA_NOALLOC_SCRATCH_BYTES (16 MiB), held until the process ends.  The call itself allocates nothing (no hipMalloc, no
+ * allocating library routine); its first call on a device looks up that
+ * device's array address once.  When the preferred split does not fit, the
+ * call uses fewer splits; CSA_ERR_TOO_LARGE when even the minimum split's
+ * partial results exceed the array.  Nothing in the array needs clearing:
+ * every partial row the merge reads is written by the same call.  All calls
+ * on one GPU share its array, which keeps the last call's contents, so
+ * calls that overlap on one GPU (different streams, or graph replays in
+ * flight together) race: serialise them. */
+int csa_decode_attn_noalloc(const uint16_t* q, int64_t q_stride,
+                            const csa_latent_cache* cache,
+                            const int32_t* topk_idx, int32_t k,
+                            const csa_swa_ring* swa, const int32_t* q_pos,
+                            const float* sink, float softmax_scale,
+                            float inv_rope_theta, int32_t B, int32_t H,
+                            uint16_t* out, float* lse, void* stream);
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* Prefill chunk: T queries of sequence `seq` (< cache->num_seqs) at
  * positions q_pos[T];

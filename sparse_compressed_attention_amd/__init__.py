@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "CsaError", "LatentCache", "SwaRing", "DecodePath", "PrefillPath", "library_path", "load_library",
     "csa_index_scores", "csa_index_scores_mxfp4", "csa_index_topk", "csa_index_topk_workspace_size", "csa_topk", "csa_topk_workspace_size", "csa_attn_workspace_size",
-    "csa_decode_attn", "csa_prefill_attn", "csa_status_string", "csa_version",
+    "csa_decode_attn", "csa_decode_attn_noalloc", "csa_prefill_attn", "csa_status_string", "csa_version",
     "csa_graph_capture_begin", "csa_graph_capture_end", "csa_graph_launch", "csa_graph_destroy", "StepGraph",
 ]
 
@@ -83,6 +83,9 @@ def load_library():
     lib.csa_decode_attn.argtypes = [vp, i64, ctypes.POINTER(_LatentCacheC), vp, i32, ctypes.POINTER(_SwaRingC),
                                     vp, vp, f32, f32, i32, i32, vp, vp, vp, sz, vp]
     lib.csa_decode_attn.restype = ctypes.c_int
+    lib.csa_decode_attn_noalloc.argtypes = [vp, i64, ctypes.POINTER(_LatentCacheC), vp, i32,
+                                            ctypes.POINTER(_SwaRingC), vp, vp, f32, f32, i32, i32, vp, vp, vp]
+    lib.csa_decode_attn_noalloc.restype = ctypes.c_int
     lib.csa_prefill_attn.argtypes = [vp, i64, ctypes.POINTER(_LatentCacheC), i32, vp, i32, vp, vp, f32, i32, i32,
                                      i32, vp, i32, vp, f32, f32, i32, vp, vp, vp, sz, vp]
     lib.csa_prefill_attn.restype = ctypes.c_int
@@ -393,6 +396,30 @@ def csa_decode_attn(q, cache: LatentCache, topk_idx, k, swa: SwaRing, q_pos, sin
         float(softmax_scale), float(inv_rope_theta), B, H, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream))
     _check("csa_decode_attn", rc)
+
+
+def csa_decode_attn_noalloc(q, cache: LatentCache, topk_idx, k, swa: SwaRing, q_pos, sink, softmax_scale, out,
+                            lse=None, stream=None, inv_rope_theta=0.0):
+    """csa_decode_attn with the split partial results in the library's
+    static scratch array (16 MiB per GPU) instead of a caller workspace:
+    allocates nothing.  Calls that overlap on one GPU race on that array."""
+    _decode_shapes(q, cache, topk_idx, k, swa, q_pos, sink, out, lse)
+    _need(q, "q", _B16, 3, contiguous=False)
+    _need(q_pos, "q_pos", _I32, 1)
+    _need(sink, "sink", _F32, 1)
+    _need(out, "out", _B16, 3)
+    if topk_idx is not None:
+        _need(topk_idx, "topk_idx", _I32, 2)
+    if lse is not None:
+        _need(lse, "lse", _F32, 2)
+    if q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [.][H][D] with contiguous heads")
+    B, H, _ = q.shape
+    cc, sc = cache.as_c(), swa.as_c()
+    rc = load_library().csa_decode_attn_noalloc(
+        _ptr(q), q.stride(0), ctypes.byref(cc), _ptr(topk_idx), int(k), ctypes.byref(sc), _ptr(q_pos), _ptr(sink),
+        float(softmax_scale), float(inv_rope_theta), B, H, _ptr(out), _ptr(lse), _stream(stream))
+    _check("csa_decode_attn_noalloc", rc)
 
 
 def csa_prefill_attn(q, cache: LatentCache, seq, topk_idx, k, swa_nope, swa_rope, swa_scale, swa_first_pos, W,

@@ -57,6 +57,8 @@
 //    ds_read_b64_tr_b8 (two reads per 16 dims, used for both terms).  Rope
 //    dims use ds_read_b64_tr_b16 and v_mfma 16x16x32 BF16 with P in BF16.
 //    P never leaves registers.
+#include <mutex>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -989,6 +991,31 @@ hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Partial-result scratch of the allocation-free decode entry point: one
+// array per GPU, held until the process ends.  In host code `scratch` is a
+// host-side stand-in, never a device address: host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+hipError_t attn_scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream) {
   if (p.D_nope == 448 && p.D_rope == 64) return launch_attn_t<448, 64>(p, stream);

@@ -139,6 +139,7 @@ const char* csa_status_string(int code) {
     case CSA_ERR_UNSUPPORTED: return "unsupported shape";
     case CSA_ERR_LAUNCH: return "kernel launch failed";
     case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_TOO_LARGE: return "partial results exceed the library's fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -350,10 +351,12 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
   return launch_status(launch_attn(p, (hipStream_t)stream));
 }
 
-int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache, const int32_t* topk_idx,
-                    int32_t k, const csa_swa_ring* swa, const int32_t* q_pos, const float* sink,
-                    float softmax_scale, float inv_rope_theta, int32_t B, int32_t H, uint16_t* out, float* lse, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+// Checks and launch of csa_decode_attn and csa_decode_attn_noalloc; the
+// scratch of the latter is resolved only once the arguments are known good.
+static int decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache, const int32_t* topk_idx,
+                       int32_t k, const csa_swa_ring* swa, const int32_t* q_pos, const float* sink,
+                       float softmax_scale, float inv_rope_theta, int32_t B, int32_t H, uint16_t* out, float* lse,
+                       void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   if (B < 0 || H < 1) return CSA_ERR_INVALID_ARG;
   if (B == 0) return CSA_OK;
   int rc = check_cache(cache);
@@ -400,7 +403,29 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache*
   p.D_nope = cache->D_nope;
   p.D_rope = cache->D_rope;
   const int64_t max_slots = (topk_idx ? (int64_t)k : (int64_t)cache->max_pages * cache->page_size) + swa->W;
+  if (use_scratch) {
+    if (attn_scratch_address(&workspace) != hipSuccess) return CSA_ERR_LAUNCH;
+    workspace_bytes = kAttnScratchBytes;
+    const int rc = run_attn(p, max_slots, workspace, workspace_bytes, stream);
+    return rc == CSA_ERR_WORKSPACE ? CSA_ERR_TOO_LARGE : rc;
+  }
   return run_attn(p, max_slots, workspace, workspace_bytes, stream);
+}
+
+int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache, const int32_t* topk_idx,
+                    int32_t k, const csa_swa_ring* swa, const int32_t* q_pos, const float* sink,
+                    float softmax_scale, float inv_rope_theta, int32_t B, int32_t H, uint16_t* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_attn(q, q_stride, cache, topk_idx, k, swa, q_pos, sink, softmax_scale, inv_rope_theta, B, H, out, lse,
+                     workspace, workspace_bytes, false, stream);
+}
+
+int csa_decode_attn_noalloc(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache,
+                            const int32_t* topk_idx, int32_t k, const csa_swa_ring* swa, const int32_t* q_pos,
+                            const float* sink, float softmax_scale, float inv_rope_theta, int32_t B, int32_t H,
+                            uint16_t* out, float* lse, void* stream) {
+  return decode_attn(q, q_stride, cache, topk_idx, k, swa, q_pos, sink, softmax_scale, inv_rope_theta, B, H, out, lse,
+                     nullptr, 0, true, stream);
 }
 
 int csa_prefill_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache, int32_t seq,

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "csa.h"
+
 namespace csa {
 
 struct IndexParams {
@@ -89,6 +91,11 @@ struct AttnParams {
   int n_hg, n_splits, per_split;
 };
 hipError_t launch_attn(const AttnParams& p, hipStream_t stream);
+// Address of the current device's copy of the library's static attention
+// scratch array (kAttnScratchBytes), looked up once per device.
+hipError_t attn_scratch_address(void** ptr);
+constexpr size_t kAttnScratchBytes = CSA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
 constexpr int kAttnMaxSlots = 2048;   // key slots one workgroup handles
 constexpr int kAttnTau = 4;           // lazy-rescale threshold (log2 units)
 constexpr int kAttnTile = 64;
