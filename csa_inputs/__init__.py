@@ -94,6 +94,11 @@ class Spec:
     with_indexer: bool = True      # False for the HCA layer (no indexer inputs)
     mxfp4: bool = False            # also store the indexer q/k in MXFP4 (same draws)
     keep_float: bool = False       # also keep the indexer q/k draws unquantised (float32)
+    # plant this many indexer keys per sequence along its query's summed
+    # index-head direction (gains U(plant_gain)), among the entries before the
+    # newest stored one: a workload whose unquantised top-k stands apart
+    plant_topk: int = 0
+    plant_gain: tuple = (1.0, 2.0)
     # prefill only: number of query tokens at the end of the single sequence
     T_prefill: int = 0
     # decode: position of each sequence's query (default ctx_len - 1)
@@ -162,6 +167,29 @@ def _draw_normal(rng, shape):
     return rng.standard_normal(shape, dtype=np.float32)
 
 
+def _plant_keys(ki, q_draws, s, n_comp, seed):
+    """Adds gain x dir_b to plant_topk keys of each decode sequence b, where
+    dir_b is the sum of query b's index-head vectors scaled to norm
+    sqrt(D_I), and the gains are U(plant_gain).  The keys are drawn among the
+    entries before the sequence's newest stored one (those a query at the
+    sequence's last position sees).  A generator of its own (seed + 7919), so
+    every other array keeps its draws."""
+    if s.kind != "decode":
+        raise ValueError("planted keys are defined for decode batches")
+    prng = np.random.default_rng(seed + 7919)
+    off = 0
+    for b in range(len(n_comp)):
+        n = int(n_comp[b])
+        if s.plant_topk > n - 1:
+            raise ValueError("more planted keys than entries")
+        d = q_draws[b].astype(np.float64).sum(axis=0)
+        d *= np.sqrt(s.D_I) / np.linalg.norm(d)
+        rows = prng.choice(n - 1, size=s.plant_topk, replace=False)
+        gains = prng.uniform(s.plant_gain[0], s.plant_gain[1], size=s.plant_topk)
+        ki[off + rows] += (gains[:, None] * d[None, :]).astype(np.float32)
+        off += n
+
+
 def generate(spec: Spec, seed: int) -> Workload:
     """Draw one workload.  Draw order (PCG64 via numpy.default_rng(seed)):
     q_idx, w, k_idx, latents, SWA rows, q, sink, page permutation."""
@@ -204,9 +232,13 @@ def generate(spec: Spec, seed: int) -> Workload:
             wl.q_idx4, wl.q_idx4_sc = mxfp4_pack(qi)
         if s.keep_float:
             wl.q_idx_f32 = qi
+        q_draws = qi
         del qi
         wl.w = rng.random((T, s.H_I), dtype=np.float32)
         ki = _draw_normal(rng, (n_entries, s.D_I))
+        if s.plant_topk:
+            _plant_keys(ki, q_draws, s, n_comp, seed)
+        del q_draws
         wl.k_idx_scale = per_tensor_scale(ki, s.unit_scale)
         ki_b = e4m3_bytes(ki, wl.k_idx_scale)
         if s.mxfp4:

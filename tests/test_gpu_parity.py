@@ -377,6 +377,36 @@ def test_indexer_recall_at_the_pages_shapes():
         assert r8 > 0.8 and r4 > 0.5
 
 
+PLANT_MARGIN = 0.03   # the stated gap: k-th >= (1 + 0.03) x (k+1)-th unquantised score, every row
+RECALL_GATE = 0.997   # "ROADMAP -- Stage E", E7: recall@k >= 99.7% vs the exact scores
+
+
+@pytest.mark.parametrize("n_comp,k", [(2048, 512), (8192, 512), (8192, 1024), (32768, 512), (32768, 1024)])
+def test_indexer_recall_gate_with_a_stated_margin(n_comp, k):
+    # The pages' recall gate, on a workload where it can be met and so can
+    # fail: k keys of every sequence are planted along its query's summed
+    # index-head direction (gains U(0.8, 1.6)), so the exact (unquantised)
+    # top-k stands apart from the rest by at least PLANT_MARGIN, checked
+    # here with the oracle.  Both the E4M3 and the MXFP4 indexer must then
+    # recover >= 99.7% of the exact top-k in every row.
+    say(f"case recall gate: {n_comp} entries, k {k}, margin >= {PLANT_MARGIN}")
+    spec = ci.Spec(name=f"planted_{n_comp}_{k}", kind="decode", ctx_lens=[4 * n_comp] * 4, k=k, mxfp4=True,
+                   keep_float=True, plant_topk=k, plant_gain=(0.8, 1.6), shuffle_pages=True)
+    wl = ci.generate(spec, seed=400 + n_comp // 1024 + k)
+    got = {"E4M3": run_gpu(wl)["topk"], "MXFP4": run_gpu(wl, mxfp4=True)["topk"]}
+    for t in range(wl.T):
+        exact = oracle.index_scores_unquantised(wl, t)
+        srt = np.sort(exact)[::-1]
+        margin = srt[k - 1] / srt[k] - 1.0
+        assert margin >= PLANT_MARGIN, f"row {t}: margin {margin:.3f} below the stated {PLANT_MARGIN}"
+        ref = oracle.topk_select(exact, k)
+        ref_set = set(ref[ref >= 0].tolist())
+        for fmt, sel in got.items():
+            rec = len(ref_set & set(sel[t][sel[t] >= 0].tolist())) / k
+            say(f"  row {t}: margin {margin:.3f}, {fmt} recall@{k} {rec:.4f}")
+            assert rec >= RECALL_GATE, f"{fmt} recall@{k} {rec:.4f} below {RECALL_GATE} (row {t})"
+
+
 @pytest.mark.parametrize("name,queries", [("c2", [0, 21, 63]), ("c3_csa", [0, 2]), ("c4", [0, 1024, 2047])])
 def test_mxfp4_indexer_full_size(name, queries):
     say(f"case MXFP4 indexer full size {name}")

@@ -150,3 +150,25 @@ def test_unquantised_draws_are_the_quantised_ones_before_rounding():
                    k=16, W=32, page_size=16, keep_float=True)
     wl = ci.generate(spec, 13)
     assert np.array_equal(ci.e4m3_bytes(wl.q_idx_f32, wl.q_idx_scale), wl.q_idx)
+
+
+def test_planted_keys_change_only_the_planted_rows():
+    # planting draws from a generator of its own: every other array keeps
+    # its draws, and exactly plant_topk keys per sequence move, none of them
+    # the newest stored entry
+    base = dict(name="pl", kind="decode", ctx_lens=[400, 260], H=8, D_nope=48, D_rope=16, H_I=4, D_I=32, k=8,
+                W=32, page_size=16, keep_float=True, shuffle_pages=True)
+    a = ci.generate(ci.Spec(**base), seed=21)
+    b = ci.generate(ci.Spec(**base, plant_topk=8, plant_gain=(0.8, 1.6)), seed=21)
+    for name in ("q_idx", "w", "lat_nope", "lat_rope", "q", "sink", "swa_nope", "page_table"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    moved = np.flatnonzero(np.any(a.k_idx_f32 != b.k_idx_f32, axis=1))
+    off = a.entry_offset
+    for s_ in range(a.B):
+        rows = moved[(moved >= off[s_]) & (moved < off[s_] + a.n_comp[s_])] - off[s_]
+        assert len(rows) == 8 and rows.max() < a.n_comp[s_] - 1
+    # the planted keys stand apart in the unquantised scores (the oracle)
+    for t in range(b.T):
+        exact = oracle.index_scores_unquantised(b, t)
+        srt = np.sort(exact)[::-1]
+        assert srt[7] > 1.05 * srt[8]
