@@ -71,6 +71,9 @@ def parse():
                     help="indexer on MXFP4 inputs (csa_index_scores_mxfp4) instead of E4M3")
     ap.add_argument("--fused-topk", action="store_true",
                     help="steps 1+2 as one call (csa_index_topk, decode only)")
+    ap.add_argument("--topk-in-attn", action="store_true",
+                    help="steps 2-4 as one call (csa_topk_decode_attn: the attention kernel selects the top-k; "
+                         "decode rows up to 8192 entries)")
     ap.add_argument("--inv-rope-theta", type=float, default=0.0,
                     help="base of the inverse-RoPE epilogue on the output's rope dims (0 = off)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -210,6 +213,11 @@ def accounting(wl, mxfp4=False):
     acc[attn] = dict(
         bytes=lat_bytes + T * s.H * s.D * 2 * 2 + T * s.H * 4 + (T * s.k * 4 if wl.q_idx is not None else 0),
         flops=4.0 * s.H * s.D * float(keys.sum()))
+    if wl.q_idx is not None and s.kind == "decode":
+        # steps 2-4 in one call: the scores are read instead of the top-k
+        # list, and the list is written once
+        acc["topk_decode_attn"] = dict(bytes=acc[attn]["bytes"] + int(nv.sum()) * 4 + T * 4,
+                                       flops=acc[attn]["flops"])
     return acc
 
 
@@ -239,7 +247,7 @@ def roofline_entry(name, a, ms, peaks=None):
 
 def kernel_source_sha(name):
     src = {"index_scores": "index_scores.hip", "topk": "topk.hip", "decode_attn": "attn.hip",
-           "prefill_attn": "attn.hip", "index_topk": "index_scores.hip"}[name]
+           "prefill_attn": "attn.hip", "index_topk": "index_scores.hip", "topk_decode_attn": "attn.hip"}[name]
     h = hashlib.sha256()
     for f in (src, "csa_device.h", "csa_internal.h", "topk_select.h"):
         with open(os.path.join(ROOT, "sparse_compressed_attention_amd", "csrc", f), "rb") as fh:
@@ -353,7 +361,7 @@ def main():
                                            (64 << 30) // max(footprint, 1))))
     theta = args.inv_rope_theta
     fp4 = args.mxfp4
-    opts = dict(inv_rope_theta=theta, mxfp4=fp4, fused_topk=args.fused_topk)
+    opts = dict(inv_rope_theta=theta, mxfp4=fp4, fused_topk=args.fused_topk, topk_in_attn=args.topk_in_attn)
     paths = [make_path(d0, **opts)] + [make_path(to_device(wl, dev), **opts) for _ in range(copies - 1)]
     del d0
     stages = paths[0].stage_names
@@ -455,7 +463,7 @@ def main():
     # the two kernels the metric names: the indexer scan and the attention
     by_kernel = {}
     for role, nm in (("indexer", "index_scores"), ("indexer", "index_topk"), ("fmha", "decode_attn"),
-                     ("fmha", "prefill_attn")):
+                     ("fmha", "prefill_attn"), ("fmha", "topk_decode_attn")):
         if nm in kernels:
             e = roofline_entry(nm, acc[nm], kernels[nm]["ms"], peaks)
             e["kernel"] = nm
@@ -472,6 +480,7 @@ def main():
                     gpu_ms_per_step=round(gpu_step, 5), launch="graph replay" if graphs else "eager calls",
                     inv_rope_theta=theta or None, indexer="MXFP4" if fp4 else "E4M3",
                     fused_topk=bool(getattr(paths[0], "fused_topk", False)),
+                    topk_in_attn=bool(getattr(paths[0], "topk_in_attn", False)),
                     synced_step_latency=latency, step_ms_spread=spread),
         roofline=roof,
         roofline_kernels=by_kernel,

@@ -8,6 +8,7 @@
  *   csa_index_topk    steps 1+2 fused, scores kept on chip
  *   csa_topk          causal top-k over those scores      (step 2)
  *   csa_decode_attn   gather + sink attention, decode     (steps 3+4)
+ *                     (csa_topk_decode_attn: steps 2-4 in one launch)
  *   csa_prefill_attn  gather + sink attention, prefill    (steps 3+4)
  * and graph capture/replay of a whole step (csa_graph_*).
  *
@@ -276,6 +277,31 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride,
                     float inv_rope_theta, int32_t B, int32_t H,
                     uint16_t* out, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode with the top-k inside the attention kernel ([Audit] B2: top-k
+ * with a wave-local reduction and no global lock; [Roadmap] E7): the result
+ * of csa_topk(scores, ld_scores, n_visible, B, k, topk_idx) followed by
+ * csa_decode_attn(..., topk_idx, k, ...), in one launch.  Every attention
+ * workgroup of query b selects its row's top-k from scores[b][0 ..
+ * n_visible[b]) itself, with csa_topk's selection rule (larger score first,
+ * equal scores to the lower index), so the indices are identical to
+ * csa_topk's; they stay on chip, and are also written to topk_idx [B][k]
+ * (ascending, -1 padding) when topk_idx is not NULL.  The other arguments,
+ * the result and the workspace (csa_attn_workspace_size with
+ * max_keys_per_query = k + W) are those of csa_decode_attn.
+ *   scores [B][ld_scores] float, n_visible [B] int32 (clamped to
+ *   [0, ld_scores]), as csa_index_scores writes them.
+ * Supported: 1 <= ld_scores <= 8192 (one workgroup holds a row) and
+ * 1 <= k <= 2048; longer rows are CSA_ERR_UNSUPPORTED (use csa_topk and
+ * csa_decode_attn).  Errors as csa_decode_attn. */
+int csa_topk_decode_attn(const float* scores, int64_t ld_scores,
+                         const int32_t* n_visible, int32_t k, int32_t* topk_idx,
+                         const uint16_t* q, int64_t q_stride,
+                         const csa_latent_cache* cache, const csa_swa_ring* swa,
+                         const int32_t* q_pos, const float* sink, float softmax_scale,
+                         float inv_rope_theta, int32_t B, int32_t H,
+                         uint16_t* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode without any allocation, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "CsaError", "LatentCache", "SwaRing", "DecodePath", "PrefillPath", "library_path", "load_library",
     "csa_index_scores", "csa_index_scores_mxfp4", "csa_index_topk", "csa_index_topk_workspace_size", "csa_topk", "csa_topk_workspace_size", "csa_attn_workspace_size",
-    "csa_decode_attn", "csa_decode_attn_noalloc", "csa_prefill_attn", "csa_status_string", "csa_version",
+    "csa_decode_attn", "csa_decode_attn_noalloc", "csa_topk_decode_attn", "csa_prefill_attn", "csa_status_string", "csa_version",
     "csa_graph_capture_begin", "csa_graph_capture_end", "csa_graph_launch", "csa_graph_destroy", "StepGraph",
 ]
 
@@ -86,6 +86,9 @@ def load_library():
     lib.csa_decode_attn_noalloc.argtypes = [vp, i64, ctypes.POINTER(_LatentCacheC), vp, i32,
                                             ctypes.POINTER(_SwaRingC), vp, vp, f32, f32, i32, i32, vp, vp, vp]
     lib.csa_decode_attn_noalloc.restype = ctypes.c_int
+    lib.csa_topk_decode_attn.argtypes = [vp, i64, vp, i32, vp, vp, i64, ctypes.POINTER(_LatentCacheC),
+                                         ctypes.POINTER(_SwaRingC), vp, vp, f32, f32, i32, i32, vp, vp, vp, sz, vp]
+    lib.csa_topk_decode_attn.restype = ctypes.c_int
     lib.csa_prefill_attn.argtypes = [vp, i64, ctypes.POINTER(_LatentCacheC), i32, vp, i32, vp, vp, f32, i32, i32,
                                      i32, vp, i32, vp, f32, f32, i32, vp, vp, vp, sz, vp]
     lib.csa_prefill_attn.restype = ctypes.c_int
@@ -422,6 +425,39 @@ def csa_decode_attn_noalloc(q, cache: LatentCache, topk_idx, k, swa: SwaRing, q_
     _check("csa_decode_attn_noalloc", rc)
 
 
+def csa_topk_decode_attn(scores, n_visible, k, q, cache: LatentCache, swa: SwaRing, q_pos, sink, softmax_scale, out,
+                         lse=None, topk_idx=None, workspace=None, stream=None, inv_rope_theta=0.0):
+    """csa_topk followed by csa_decode_attn in one launch: the attention
+    kernel selects each query's top-k from scores [B][ld] (rows up to 8192
+    entries) itself; topk_idx [B][k], when given, receives the indices."""
+    _need(scores, "scores", _F32, 2, contiguous=False)
+    _need(n_visible, "n_visible", _I32, 1)
+    if scores.stride(1) != 1:
+        raise ValueError("scores rows must be contiguous")
+    _decode_shapes(q, cache, topk_idx, k, swa, q_pos, sink, out, lse)
+    B = q.shape[0]
+    if scores.shape[0] != B or n_visible.shape[0] != B:
+        raise ValueError(f"scores {tuple(scores.shape)} / n_visible {tuple(n_visible.shape)} need {B} rows")
+    _need(q, "q", _B16, 3, contiguous=False)
+    _need(q_pos, "q_pos", _I32, 1)
+    _need(sink, "sink", _F32, 1)
+    _need(out, "out", _B16, 3)
+    if topk_idx is not None:
+        _need(topk_idx, "topk_idx", _I32, 2)
+    if lse is not None:
+        _need(lse, "lse", _F32, 2)
+    if q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [.][H][D] with contiguous heads")
+    H = q.shape[1]
+    cc, sc = cache.as_c(), swa.as_c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().csa_topk_decode_attn(
+        _ptr(scores), scores.stride(0), _ptr(n_visible), int(k), _ptr(topk_idx), _ptr(q), q.stride(0),
+        ctypes.byref(cc), ctypes.byref(sc), _ptr(q_pos), _ptr(sink), float(softmax_scale), float(inv_rope_theta), B,
+        H, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("csa_topk_decode_attn", rc)
+
+
 def csa_prefill_attn(q, cache: LatentCache, seq, topk_idx, k, swa_nope, swa_rope, swa_scale, swa_first_pos, W,
                      q_pos, sink, softmax_scale, out, lse=None, workspace=None, stream=None, inv_rope_theta=0.0):
     _prefill_shapes(q, cache, seq, topk_idx, k, swa_nope, swa_rope, q_pos, sink, out, lse)
@@ -502,12 +538,15 @@ class DecodePath(_Path):
 
     def __init__(self, *, cache: LatentCache, swa: SwaRing, q, q_pos, sink, softmax_scale, k,
                  q_idx=None, q_idx_scale=1.0, w=None, k_idx=None, k_idx_scale=1.0, inv_rope_theta=0.0,
-                 q_idx_sc=None, k_idx_sc=None, fused_topk=False):
+                 q_idx_sc=None, k_idx_sc=None, fused_topk=False, topk_in_attn=False):
         dev = q.device
         self.inv_rope_theta = float(inv_rope_theta)
         self.q_idx_sc, self.k_idx_sc = q_idx_sc, k_idx_sc   # both given: MXFP4 indexer inputs
         # steps 1+2 as one call that keeps the scores on chip (E4M3 only)
         self.fused_topk = bool(fused_topk) and q_idx is not None and q_idx_sc is None
+        # steps 2-4 as one call (csa_topk_decode_attn): the attention kernel
+        # selects the top-k from the scores (rows up to 8192 entries)
+        self.topk_in_attn = bool(topk_in_attn) and q_idx is not None and not self.fused_topk
         self.cache, self.swa, self.q, self.q_pos, self.sink = cache, swa, q, q_pos, sink
         self.softmax_scale, self.k = float(softmax_scale), int(k)
         self.q_idx, self.q_idx_scale, self.w, self.k_idx, self.k_idx_scale = q_idx, q_idx_scale, w, k_idx, k_idx_scale
@@ -521,7 +560,13 @@ class DecodePath(_Path):
         if q_idx is not None:
             self.n_vis = torch.empty((B,), dtype=torch.int32, device=dev)
             self.topk = torch.empty((B, self.k), dtype=torch.int32, device=dev)
-            if self.fused_topk:
+            if self.topk_in_attn and self.ld > 8192:
+                raise ValueError("the top-k inside the attention takes rows of at most 8192 entries")
+            if self.topk_in_attn:
+                self.scores = torch.empty((B, self.ld), dtype=torch.float32, device=dev)
+                tw = 0
+                self.stage_names = ("index_scores", "topk_decode_attn")
+            elif self.fused_topk:
                 self.scores = None
                 tw = csa_index_topk_workspace_size(B, max_entries, self.k)
                 self.stage_names = ("index_topk", "decode_attn")
@@ -557,6 +602,8 @@ class DecodePath(_Path):
                     float(self.k_idx_scale), _ptr(pt), _ptr(self.cache.n_comp), P, ps, pt.shape[1], pt.shape[0],
                     _ptr(self.q_pos), _ptr(self.q_seq), T, H_I, D_I, int(self.cache.ratio_m), self.k,
                     _ptr(self.topk), _ptr(self.n_vis), _ptr(self.topk_ws), tw)))
+            elif self.topk_in_attn:
+                plan.append(self._index_stage())
             else:
                 plan.append(self._index_stage())
                 plan.append(("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), B, self.k, _ptr(self.topk),
@@ -565,6 +612,13 @@ class DecodePath(_Path):
         _need(self.q_pos, "q_pos", _I32, 1)
         _need(self.sink, "sink", _F32, 1)
         aw = 0 if self.attn_ws is None else self.attn_ws.numel()
+        if self.topk_in_attn:
+            plan.append(("csa_topk_decode_attn", (
+                _ptr(self.scores), self.ld, _ptr(self.n_vis), self.k, _ptr(self.topk), _ptr(self.q), self.q.stride(0),
+                ctypes.byref(self._cc), ctypes.byref(self._sc), _ptr(self.q_pos), _ptr(self.sink),
+                self.softmax_scale, self.inv_rope_theta, B, H, _ptr(self.out), _ptr(self.lse), _ptr(self.attn_ws),
+                aw)))
+            return plan
         plan.append(("csa_decode_attn", (
             _ptr(self.q), self.q.stride(0), ctypes.byref(self._cc), _ptr(self.topk), self.k, ctypes.byref(self._sc),
             _ptr(self.q_pos), _ptr(self.sink), self.softmax_scale, self.inv_rope_theta, B, H, _ptr(self.out),

@@ -61,6 +61,7 @@
 
 #include "csa_device.h"
 #include "csa_internal.h"
+#include "topk_select.h"
 
 namespace csa {
 
@@ -167,7 +168,7 @@ struct Block {
 
 template <int DN, int DR, int DP, int HT, int ND>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, uint8_t* xs0, int32_t* desc,
-                                          v4f* sx, v2i* pxh, v2i* pxb, int wave) {
+                                          v4f* sx, v2i* pxh, v2i* pxb, int wave, const int32_t* sel) {
   using C = Cfg<DN, DR>;
   using HF = Part<DN, DR, ND, DP>;
   constexpr int D = DN + DR;
@@ -224,7 +225,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     int v = -1;
     if (s < nkeys) {
       if (slot < n_sel) {
-        v = p.topk ? p.topk[(size_t)t * p.k + slot] : slot;
+        v = sel ? sel[slot] : p.topk ? p.topk[(size_t)t * p.k + slot] : slot;
       } else if (slot >= sel_end && !prefill) {
         v = p.swa_pos[(size_t)seq * p.W + (slot - sel_end)];
       }
@@ -833,7 +834,11 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 template <int DN, int DR, int HT, int ND>
 __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   using C = Cfg<DN, DR>;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kNBuf * C::TILE_BYTES];
+  // the tile ring (also the selection histograms of csa_topk_decode_attn
+  // before the first tile, which need more than the small tiles' ring)
+  constexpr size_t kRing = (size_t)kNBuf * C::TILE_BYTES;
+  constexpr size_t kSelHist = sizeof(topk_sel::TopkShared<64 * ND * HT>);
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kRing > kSelHist ? kRing : (kSelHist + 15) / 16 * 16];
   __shared__ int32_t desc[kAttnMaxSlots];
   __shared__ v4f sx[ND * HT * 4 * 64];   // partial score tiles, [wave][subtile][lane]
   // each part's subtiles of P: E4M3 hi/lo [wave][subtile][lane]; BF16 of the
@@ -867,7 +872,7 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   bk.nc = p.n_comp[bk.seq];
   // with a top-k list the slot count needs nothing loaded, so the
   // descriptor loads need not wait for the position
-  if (p.topk) {
+  if (p.topk || p.scores) {
     bk.n_sel = p.k;
   } else {
     bk.n_sel = bk.pos >= 0 ? max(0, min(bk.pos / p.ratio_m, bk.nc)) : 0;
@@ -880,22 +885,73 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   if (bk.split > 0 && bk.kv0 >= n_slots) return;   // empty split: the merge skips it
   bk.nkeys = max(0, min(n_slots, bk.kv0 + p.per_split) - bk.kv0);
 
+  // ---- top-k from the indexer scores (csa_topk_decode_attn): the
+  // workgroup selects its query's top-k itself, with the top-k kernels'
+  // radix selection (the same rule, so the same indices).  The histograms
+  // live in the tile ring and the indices in the score-exchange buffer,
+  // which hold nothing yet.
+  const int32_t* sel = nullptr;
+  if (p.scores) {
+    using namespace topk_sel;
+    constexpr int kThreads = 64 * ND * HT;
+    constexpr int kSelSeg = kAttnSelMax / kThreads;
+    static_assert(sizeof(TopkShared<kThreads>) <= sizeof(xs), "selection histograms fit the tile ring");
+    static_assert(kTopkMaxK * sizeof(int32_t) <= sizeof(sx), "selected indices fit the exchange buffer");
+    auto& shs = *reinterpret_cast<TopkShared<kThreads>*>(xs);
+    int32_t* selw = reinterpret_cast<int32_t*>(sx);
+    const int t = bk.t;
+    const int i0 = threadIdx.x * kSelSeg;
+    const float* src = p.scores + (size_t)t * p.ld_scores + i0;
+    const int nv_raw = p.n_visible[t];
+    // loaded without waiting for the visible count; columns past it are
+    // masked below
+    const int avail = (int)max<int64_t>(0, min<int64_t>(kSelSeg, p.ld_scores - i0));
+    uint32_t key[kSelSeg];
+    if (avail == kSelSeg && ((((uintptr_t)src) & 15) == 0)) {
+#pragma unroll
+      for (int j = 0; j < kSelSeg; j += 4) {
+        const v4f v = *reinterpret_cast<const v4f*>(src + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[j + e] = float_order_key(v[e]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelSeg; ++j) key[j] = j < avail ? float_order_key(src[j]) : 0u;
+    }
+    const int n = (int)max<int64_t>(0, min<int64_t>(nv_raw, p.ld_scores));
+    const int cnt = max(0, min(kSelSeg, n - i0));
+    const uint32_t valid = cnt >= 32 ? 0xffffffffu : ((1u << cnt) - 1u);
+    const int K = min(p.k, n);
+    if (K > 0) {
+      const Sel sl = radix_select<kThreads, kSelSeg>(key, valid, K, shs);
+      emit_selected<kThreads, kSelSeg>(key, valid, sl, shs, [&](int rank, int j) {
+        if (rank < K) selw[rank] = i0 + j;
+      });
+    }
+    for (int i = K + threadIdx.x; i < p.k; i += kThreads) selw[i] = -1;
+    __syncthreads();
+    // one workgroup of the query also hands the indices to the caller
+    if (p.topk_out && bk.hg == 0 && bk.split == 0)
+      for (int i = threadIdx.x; i < p.k; i += kThreads) p.topk_out[(size_t)t * p.k + i] = selw[i];
+    sel = selw;
+  }
+
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   __builtin_assume(wave >= 0 && wave < ND * HT);
   if constexpr (ND == 4) {
     if (wave >= 3 * HT)
-      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
+      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else if (wave >= 2 * HT)
-      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
+      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
   } else {
     if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
+      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave);
+      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
   }
 }
 
@@ -920,7 +976,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int seq = prefill ? p.prefill_seq : t;
   const int pos = p.q_pos[t];
   const int nv = pos >= 0 ? max(0, min(pos / p.ratio_m, p.n_comp[seq])) : 0;
-  const int n_slots = (((p.topk ? p.k : nv) + kAttnTile - 1) & ~(kAttnTile - 1)) + p.W;
+  const int n_slots = (((p.topk || p.scores ? p.k : nv) + kAttnTile - 1) & ~(kAttnTile - 1)) + p.W;
   const int used = max(1, min(p.n_splits, (n_slots + p.per_split - 1) / p.per_split));
   const size_t pstride = (size_t)p.T * p.H * RS;   // one split
   const float* row = p.part + ((size_t)t * p.H + h) * RS;

@@ -353,10 +353,20 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
 
 // Checks and launch of csa_decode_attn and csa_decode_attn_noalloc; the
 // scratch of the latter is resolved only once the arguments are known good.
+// The top-k scores of csa_topk_decode_attn (the selection runs inside the
+// attention kernel); nullptr scores for the other decode calls.
+struct FusedTopk {
+  const float* scores = nullptr;
+  int64_t ld = 0;
+  const int32_t* n_visible = nullptr;
+  int32_t* topk_out = nullptr;
+};
+
 static int decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache, const int32_t* topk_idx,
                        int32_t k, const csa_swa_ring* swa, const int32_t* q_pos, const float* sink,
                        float softmax_scale, float inv_rope_theta, int32_t B, int32_t H, uint16_t* out, float* lse,
-                       void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
+                       void* workspace, size_t workspace_bytes, bool use_scratch, void* stream,
+                       const FusedTopk& ft = FusedTopk()) {
   if (B < 0 || H < 1) return CSA_ERR_INVALID_ARG;
   if (B == 0) return CSA_OK;
   int rc = check_cache(cache);
@@ -380,6 +390,10 @@ static int decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cac
   p.page_table = cache->page_table;
   p.n_comp = cache->n_comp;
   p.topk = topk_idx;
+  p.scores = ft.scores;
+  p.ld_scores = ft.ld;
+  p.n_visible = ft.n_visible;
+  p.topk_out = ft.topk_out;
   p.swa_nope = swa->nope;
   p.swa_rope = swa->rope;
   p.swa_pos = swa->pos;
@@ -395,14 +409,15 @@ static int decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cac
   p.page_size = cache->page_size;
   p.max_pages = cache->max_pages;
   p.ratio_m = cache->ratio_m;
-  p.k = topk_idx ? k : 0;
+  p.k = (topk_idx || ft.scores) ? k : 0;
   p.W = swa->W;
   p.prefill_seq = -1;
   p.T = B;
   p.H = H;
   p.D_nope = cache->D_nope;
   p.D_rope = cache->D_rope;
-  const int64_t max_slots = (topk_idx ? (int64_t)k : (int64_t)cache->max_pages * cache->page_size) + swa->W;
+  const int64_t max_slots =
+      ((topk_idx || ft.scores) ? (int64_t)k : (int64_t)cache->max_pages * cache->page_size) + swa->W;
   if (use_scratch) {
     if (attn_scratch_address(&workspace) != hipSuccess) return CSA_ERR_LAUNCH;
     workspace_bytes = kAttnScratchBytes;
@@ -418,6 +433,24 @@ int csa_decode_attn(const uint16_t* q, int64_t q_stride, const csa_latent_cache*
                     size_t workspace_bytes, void* stream) {
   return decode_attn(q, q_stride, cache, topk_idx, k, swa, q_pos, sink, softmax_scale, inv_rope_theta, B, H, out, lse,
                      workspace, workspace_bytes, false, stream);
+}
+
+int csa_topk_decode_attn(const float* scores, int64_t ld_scores, const int32_t* n_visible, int32_t k,
+                         int32_t* topk_idx, const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache,
+                         const csa_swa_ring* swa, const int32_t* q_pos, const float* sink, float softmax_scale,
+                         float inv_rope_theta, int32_t B, int32_t H, uint16_t* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (B < 0) return CSA_ERR_INVALID_ARG;
+  if (B == 0) return CSA_OK;
+  if (!scores || !n_visible || ld_scores < 1) return CSA_ERR_INVALID_ARG;
+  if (k < 1 || k > kTopkMaxK || ld_scores > kAttnSelMax) return CSA_ERR_UNSUPPORTED;
+  FusedTopk ft;
+  ft.scores = scores;
+  ft.ld = ld_scores;
+  ft.n_visible = n_visible;
+  ft.topk_out = topk_idx;
+  return decode_attn(q, q_stride, cache, nullptr, k, swa, q_pos, sink, softmax_scale, inv_rope_theta, B, H, out, lse,
+                     workspace, workspace_bytes, false, stream, ft);
 }
 
 int csa_decode_attn_noalloc(const uint16_t* q, int64_t q_stride, const csa_latent_cache* cache,

@@ -60,6 +60,13 @@ struct AttnParams {
   const int32_t* page_table;
   const int32_t* n_comp;
   const int32_t* topk;     // [T][k] or nullptr (all visible entries)
+  // top-k selected inside the attention kernel (csa_topk_decode_attn):
+  // indexer scores [T][ld_scores] and visible counts [T], or nullptr;
+  // topk_out [T][k] receives the indices (nullable)
+  const float* scores;
+  int64_t ld_scores;
+  const int32_t* n_visible;
+  int32_t* topk_out;
   const uint8_t* swa_nope;
   const uint16_t* swa_rope;
   const int32_t* swa_pos;  // ring positions [B][W] (decode) or nullptr (prefill)
@@ -97,6 +104,7 @@ hipError_t attn_scratch_address(void** ptr);
 constexpr size_t kAttnScratchBytes = CSA_NOALLOC_SCRATCH_BYTES;
 constexpr int kMaxDevices = 64;
 constexpr int kAttnMaxSlots = 2048;   // key slots one workgroup handles
+constexpr int kAttnSelMax = 8192;     // longest score row the attention kernel selects from
 constexpr int kAttnTau = 4;           // lazy-rescale threshold (log2 units)
 constexpr int kAttnTile = 64;
 constexpr int kAttnMaxSplits = 128;   // splits of one query's key slots

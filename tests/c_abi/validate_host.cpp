@@ -234,6 +234,38 @@ static void index_plans(Rng& rng) {
   }
 }
 
+// Steps 2-4 in one call: rows up to 8192 scores, k up to 2048; the
+// attention plan is csa_decode_attn's with k selected slots.
+static void topk_attention_plans(Rng& rng) {
+  for (int iter = 0; iter < 2000; ++iter) {
+    const int B = (int)rng.range(1, 600);
+    const int H = 128, dn = 448, dr = 64, D = dn + dr;
+    const int64_t ld = rng.range(1, 9000);
+    const int k = (int)rng.range(1, 2100);
+    const int W = (int)rng.range(1, 1024);
+    csa_latent_cache cache{(const uint8_t*)dev(60), (const uint16_t*)dev(61), 0.7f, (const int32_t*)dev(62),
+                           (const int32_t*)dev(63), B, 4096, 64, 128, dn, dr, 4};
+    csa_swa_ring ring{(const uint8_t*)dev(64), (const uint16_t*)dev(65), 0.3f, (const int32_t*)dev(66), W};
+    const bool ok_shape = ld <= kAttnSelMax && k <= kTopkMaxK;
+    const size_t ws = ok_shape ? csa_attn_workspace_size(B, H, dn, dr, k + W) : 0;
+    const int n0 = g_stub.n_attn;
+    const int rc = csa_topk_decode_attn((const float*)dev(67), ld, (const int32_t*)dev(68), k, (int32_t*)dev(69),
+                                        (const uint16_t*)dev(70), (int64_t)H * D, &cache, &ring,
+                                        (const int32_t*)dev(71), (const float*)dev(72), 0.04f, 0.f, B, H,
+                                        (uint16_t*)dev(73), nullptr, ws ? dev(74) : nullptr, ws, nullptr);
+    if (!ok_shape) {
+      CHECK(rc == CSA_ERR_UNSUPPORTED && g_stub.n_attn == n0, "ld %lld k %d rc %d", (long long)ld, k, rc);
+      continue;
+    }
+    CHECK(rc == CSA_OK, "rc %d", rc);
+    if (rc != CSA_OK) continue;
+    const AttnParams& a = g_stub.attn;
+    CHECK(a.scores == dev(67) && a.ld_scores == ld && a.topk == nullptr && a.k == k && a.topk_out == dev(69),
+          "fused top-k parameters");
+    CHECK((int64_t)a.n_splits * a.per_split >= round_up(k, kAttnTile) + W, "fused split covers the slots");
+  }
+}
+
 int main() {
   Rng rng{20260};
   invalid_arguments();
@@ -241,6 +273,7 @@ int main() {
   attention_plans(rng, true);
   topk_plans(rng);
   index_plans(rng);
+  topk_attention_plans(rng);
   printf("host ABI checks: %d failures (attention launches %d, top-k %d, indexer %d, fused %d)\n", g_fail,
          g_stub.n_attn, g_stub.n_topk, g_stub.n_index, g_stub.n_index_topk);
   return g_fail ? 1 : 0;

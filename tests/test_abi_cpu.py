@@ -249,3 +249,16 @@ def test_prefill_binding_rejects_mismatched_shapes(change, match):
 def test_prefill_binding_shape_check_passes_consistent_shapes():
     with pytest.raises(ValueError, match="GPU tensor"):
         csa.csa_prefill_attn(**_prefill_args())
+
+
+def test_topk_in_attention_rejects_long_rows_before_launch(lib):
+    # one attention workgroup holds a row of at most 8192 scores
+    fake = ctypes.c_void_p(1 << 20)
+    cache = csa._LatentCacheC(1 << 20, 1 << 20, 1.0, 1 << 20, 1 << 20, 2, 8, 64, 4, 448, 64, 4)
+    ring = csa._SwaRingC(1 << 20, 1 << 20, 1.0, 1 << 20, 128)
+    args = (fake, 512 * 128, ctypes.byref(cache), ctypes.byref(ring), fake, fake, 1.0, 0.0, 2, 128, fake, None,
+            None, 0, None)
+    assert lib.csa_topk_decode_attn(fake, 8193, fake, 512, None, *args) == -2
+    assert lib.csa_topk_decode_attn(fake, 8192, fake, 4096, None, *args) == -2     # k > 2048
+    assert lib.csa_topk_decode_attn(None, 8192, fake, 512, None, *args) == -1      # no scores
+    assert lib.csa_topk_decode_attn(fake, 8192, None, 512, None, *args) == -1      # no visible counts

@@ -695,3 +695,79 @@ def test_topk_all_equals_hca_mode():
         o_ref, l_ref = P.reference_attention_on(wl, t, None)
         P.check_attention(oh[t], lh[t], o_ref, l_ref)
         say(f"  query {t}: {int(nv[t])} visible, top-k vs HCA max|diff| {err:.2e}, min cos {cos:.6f}")
+
+
+# --------------------------------------------------------------- top-k inside the attention
+@pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "tiny_dims_wide", "poisoned", "c1", "c2",
+                                  "k2048", "empty_rows"])
+def test_topk_in_attention_equals_separate_calls(case):
+    # csa_topk_decode_attn selects each row's top-k inside the attention
+    # kernel with csa_topk's rule: the indices must be bit-identical to
+    # csa_topk's and the outputs bit-identical to csa_decode_attn on them
+    # (same kernels, same key slots); both are also gated against the oracle
+    say(f"case top-k inside the attention: {case}")
+    qs = None
+    if case in ("c0", "c1", "c2"):
+        wl = ci.make_config(case)
+        qs = {"c2": [0, 31, 63]}.get(case)
+    elif case == "small_ragged":
+        wl = ci.generate(ci.small_spec(shuffle_pages=True), seed=351)
+    elif case == "many_sequences":
+        spec = ci.small_spec(ctx_lens=[4096, 2052, 2500, 3332, 1028, 4100, 2600, 9000], shuffle_pages=True, k=384)
+        wl = ci.generate(spec, seed=352)
+    elif case == "tiny_dims_wide":
+        rng = np.random.default_rng(353)
+        lens = [int(x) * 4 for x in rng.integers(40, 160, size=300)]
+        spec = ci.Spec(name="tiny_decode_300", kind="decode", ctx_lens=lens, H=8, D_nope=48, D_rope=16, H_I=4,
+                       D_I=32, k=16, W=32, page_size=16, shuffle_pages=True)
+        wl, qs = ci.generate(spec, seed=353), [0, 1, 150, 299]
+    elif case == "k2048":
+        wl = ci.generate(ci.small_spec(name="small_k2048", ctx_lens=[12000, 3000, 620], k=2048, shuffle_pages=True),
+                         seed=354)
+    elif case == "empty_rows":
+        # rows with nothing visible (no stored entry, or a position in the
+        # first block): all -1 indices, the window alone is attended
+        wl = ci.generate(ci.small_spec(ctx_lens=[3000, 1508, 2400, 700], shuffle_pages=True), seed=355)
+        n_comp = wl.n_comp.copy()
+        n_comp[1] = 0
+        q_pos = wl.q_pos.copy()
+        q_pos[3] = 2
+        wl = dataclasses.replace(wl, n_comp=n_comp, q_pos=q_pos)
+    else:
+        # own and future blocks made the strongest keys: never selected
+        wl = ci.generate(ci.small_spec(ctx_lens=[3000, 2400], shuffle_pages=True), seed=356)
+        s = wl.spec
+        k_idx = wl.k_idx.copy()
+        for b in range(wl.B):
+            nv = oracle.n_visible(int(wl.q_pos[b]), s.m, int(wl.n_comp[b]))
+            for c in range(nv, int(wl.n_comp[b])):
+                page = int(wl.page_table[b][c // s.page_size])
+                k_idx[page, c % s.page_size] = wl.q_idx[b][0]
+        wl = dataclasses.replace(wl, k_idx=k_idx)
+    d = to_device(wl, "cuda")
+    three = make_path(d)
+    fused = make_path(d, topk_in_attn=True)
+    assert fused.stage_names == ("index_scores", "topk_decode_attn")
+    three.run()
+    for rep in range(2):
+        fused.topk.fill_(-7)
+        fused.out.fill_(5.0)
+        fused.run()
+        torch.cuda.synchronize()
+        assert torch.equal(three.topk, fused.topk), f"call {rep}: indices differ"
+        assert torch.equal(three.out.view(torch.int16), fused.out.view(torch.int16)), f"call {rep}: outputs differ"
+        assert torch.equal(three.lse, fused.lse)
+    topk = fused.topk.cpu().numpy()
+    o = P.bf16_to_f64(fused.out)
+    lv = fused.lse.cpu().numpy().astype(np.float64)
+    worst = (0.0, 1.0)
+    for t in (range(wl.T) if qs is None else qs):
+        ref_scores = oracle.index_scores(wl, t)
+        P.check_topk_vs_oracle(topk[t], ref_scores, wl.spec.k)
+        if case == "poisoned":
+            nv = oracle.n_visible(int(wl.q_pos[t]), wl.spec.m, int(wl.n_comp[int(wl.q_seq[t])]))
+            assert (topk[t] < nv).all()
+        o_ref, l_ref = P.reference_attention_on(wl, t, topk[t])
+        err, cos = P.check_attention(o[t], lv[t], o_ref, l_ref)
+        worst = (max(worst[0], err), min(worst[1], cos))
+    say(f"  {case}: identical to csa_topk + csa_decode_attn; max|err| {worst[0]:.3e} min cos {worst[1]:.6f}")
