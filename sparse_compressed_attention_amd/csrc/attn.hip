@@ -770,7 +770,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
 
   // ---- output of this part's dims (the softmax state is the same in every part)
   const bool final_out = p.n_splits == 1;
-  const float invL = (final_out && L > 0.0f) ? 1.0f / L : 0.0f;
+  const float invL = L > 0.0f ? 1.0f / L : 0.0f;
   // inverse RoPE of the rope dims at the query position, when this
   // workgroup writes the final output (split outputs are rotated by the
   // merge).  Lane i < DR / 2 forms the rotation of pair i; every lane then
@@ -806,18 +806,20 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
           v = (v4f){a.x, a.y, b.x, b.y};
         }
       }
+      // the final output, or this split's output normalised by its own
+      // denominator (BF16, like the output; the merge weighs it by L)
+      const v2i pk = (v2i){(int)pack2_bf16(v[0] * invL, v[1] * invL), (int)pack2_bf16(v[2] * invL, v[3] * invL)};
       if (final_out) {
-        const v2i pk = (v2i){(int)pack2_bf16(v[0] * invL, v[1] * invL), (int)pack2_bf16(v[2] * invL, v[3] * invL)};
         *reinterpret_cast<v2i*>(p.out + ((size_t)t * p.H + h) * D + dim) = pk;
       } else {
-        *reinterpret_cast<v4f*>(p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + kPartPad) + dim) = v;
+        *reinterpret_cast<v2i*>(p.part + (((size_t)bk.split * p.T + t) * p.H + h) * part_row_bytes(D) + 2 * dim) = pk;
       }
     }
     if (DP == 0 && g == 0) {
       if (final_out) {
         if (p.lse) p.lse[(size_t)t * p.H + h] = (L > 0.0f) ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
       } else {
-        float* dst = p.part + (((size_t)bk.split * p.T + t) * p.H + h) * (D + kPartPad) + D;
+        float* dst = reinterpret_cast<float*>(p.part + (((size_t)bk.split * p.T + t) * p.H + h) * part_row_bytes(D) + 2 * D);
         dst[0] = M;
         dst[1] = L;
       }
@@ -955,16 +957,17 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   }
 }
 
-// Combines the per-split partial states (unnormalised O, running max in log2
-// units, denominator) of every (query, head) into the output and lse.  128
-// threads per (query, head): the split weights exp2(M_s - M) are computed
-// once into LDS (thread s owns split s), then thread i sums dims
-// [4 i, 4 i + 4) over the splits with 16-byte loads.
+// Combines the per-split partial states (the split's output normalised by
+// its denominator, in BF16; running max in log2 units; denominator) of every
+// (query, head) into the output and lse.  128 threads per (query, head): the
+// split weights L_s exp2(M_s - M) are computed once into LDS (thread s owns
+// split s), then thread i sums dims [4 i, 4 i + 4) over the splits with
+// 8-byte loads.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   __shared__ float wgt[2][kAttnMaxSplits];
   __shared__ float red[2][2][2];
   const int D = p.D_nope + p.D_rope;
-  const int RS = D + kPartPad;
+  const size_t RB = part_row_bytes(D);
   const int half = threadIdx.x >> 7;          // pair of this thread within the workgroup
   const int sub = threadIdx.x & 127;
   const int wv = (threadIdx.x >> 6) & 1;      // wave within the pair
@@ -978,14 +981,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int nv = pos >= 0 ? max(0, min(pos / p.ratio_m, p.n_comp[seq])) : 0;
   const int n_slots = (((p.topk || p.scores ? p.k : nv) + kAttnTile - 1) & ~(kAttnTile - 1)) + p.W;
   const int used = max(1, min(p.n_splits, (n_slots + p.per_split - 1) / p.per_split));
-  const size_t pstride = (size_t)p.T * p.H * RS;   // one split
-  const float* row = p.part + ((size_t)t * p.H + h) * RS;
+  const size_t pstride = (size_t)p.T * p.H * RB;   // one split (bytes)
+  const uint8_t* row = p.part + ((size_t)t * p.H + h) * RB;
 
   // split weights and the merged max / denominator
   float m = -__builtin_inff(), l = 0.0f;
   if (pair_ok && sub < used) {
-    m = row[sub * pstride + D];
-    l = row[sub * pstride + D + 1];
+    const float2 ml = *reinterpret_cast<const float2*>(row + sub * pstride + 2 * D);
+    m = ml.x;
+    l = ml.y;
   }
   float mm = m;
 #pragma unroll
@@ -995,8 +999,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const float M = fmaxf(red[half][0][0], red[half][0][1]);
   const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
   const float a = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Ms);
-  if (sub < kAttnMaxSplits) wgt[half][sub] = a;
   float la = l * a;
+  if (sub < kAttnMaxSplits) wgt[half][sub] = la;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) la += __shfl_xor(la, off, 64);
   if ((threadIdx.x & 63) == 0) red[half][1][wv] = la;
@@ -1006,16 +1010,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const float invL = L > 0.0f ? 1.0f / L : 0.0f;
   const int d0 = 4 * sub;
   if (d0 < D) {
+    auto unpack = [](v2i w) -> v4f {
+      return (v4f){__uint_as_float((uint32_t)w[0] << 16), __uint_as_float((uint32_t)w[0] & 0xffff0000u),
+                   __uint_as_float((uint32_t)w[1] << 16), __uint_as_float((uint32_t)w[1] & 0xffff0000u)};
+    };
     v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
     int s = 0;
     for (; s + 4 <= used; s += 4) {
-      v4f v[4];
+      v2i v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const v4f*>(row + (s + j) * pstride + d0);
+      for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const v2i*>(row + (s + j) * pstride + 2 * d0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc += v[j] * wgt[half][s + j];
+      for (int j = 0; j < 4; ++j) acc += unpack(v[j]) * wgt[half][s + j];
     }
-    for (; s < used; ++s) acc += *reinterpret_cast<const v4f*>(row + s * pstride + d0) * wgt[half][s];
+    for (; s < used; ++s) acc += unpack(*reinterpret_cast<const v2i*>(row + s * pstride + 2 * d0)) * wgt[half][s];
     if (d0 >= p.D_nope && p.inv_rope) {
       // inverse RoPE of rope pairs (d0 - D_nope) / 2 and the next one
       const int pr = (d0 - p.D_nope) >> 1;

@@ -73,7 +73,7 @@ struct AttnPlan {
   size_t ws_bytes = 0;
 };
 size_t partial_bytes(int64_t T, int64_t H, int D, int splits) {
-  return (size_t)splits * (size_t)T * (size_t)H * (size_t)(D + kPartPad) * sizeof(float);
+  return (size_t)splits * (size_t)T * (size_t)H * part_row_bytes(D);
 }
 // Preferred plan, then shrunk to what `ws_avail` holds.  Returns false when
 // even the minimum number of splits does not fit.
@@ -345,7 +345,7 @@ static int run_attn(AttnParams& p, int64_t max_slots, void* workspace, size_t wo
   p.n_hg = pl.n_hg;
   p.n_splits = pl.n_splits;
   p.per_split = pl.per_split;
-  p.part = pl.n_splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  p.part = pl.n_splits > 1 ? static_cast<uint8_t*>(workspace) : nullptr;
   const int64_t blocks = (p.T >= 8 ? ceil_div(p.T, 8) * 8 : (int64_t)p.T) * p.n_hg * p.n_splits;
   if (blocks >= ((int64_t)1 << 31)) return CSA_ERR_UNSUPPORTED;
   return launch_status(launch_attn(p, (hipStream_t)stream));

@@ -74,7 +74,10 @@ struct AttnParams {
   const float* sink;
   uint16_t* out;
   float* lse;
-  float* part;             // [n_splits][T][H][D + kPartPad] or nullptr: O, then (M, L) at D, D + 1
+  // split partial results or nullptr: rows of part_row_bytes(D) bytes,
+  // [n_splits][T][H]: the split's output over its denominator as D BF16,
+  // then (M, L) as two floats, then padding to 16 bytes
+  uint8_t* part;
   float lat_scale, swa_scale;
   float sm_scale;          // softmax scale (natural-log units)
   // derived on the host (uniform): sm_scale*log2(e); FP8 probability scale
@@ -108,6 +111,7 @@ constexpr int kAttnSelMax = 8192;     // longest score row the attention kernel 
 constexpr int kAttnTau = 4;           // lazy-rescale threshold (log2 units)
 constexpr int kAttnTile = 64;
 constexpr int kAttnMaxSplits = 128;   // splits of one query's key slots
-constexpr int kPartPad = 4;           // partial rows padded to 16 bytes
+// bytes of one split partial row: D BF16 values, (M, L), 16-byte aligned
+__host__ __device__ constexpr size_t part_row_bytes(int D) { return (size_t)2 * D + 16; }
 
 }  // namespace csa

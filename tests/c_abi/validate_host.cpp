@@ -125,7 +125,7 @@ static void attention_plans(Rng& rng, bool prefill) {
           (long long)need_slots);
     CHECK((a.n_splits == 1) == (a.part == nullptr), "partials pointer");
     CHECK((a.ht == 2 || a.ht == 4) && a.n_hg * 16 * a.ht >= H, "head groups");
-    const uint64_t part_bytes = (uint64_t)a.n_splits * T * H * (D + kPartPad) * 4;
+    const uint64_t part_bytes = (uint64_t)a.n_splits * T * H * part_row_bytes(D);
     CHECK(a.n_splits == 1 || part_bytes <= ws, "partials %llu > workspace %zu", (unsigned long long)part_bytes, ws);
     // half the workspace: a coarser split that fits, or refused
     if (ws > 0) {
@@ -134,7 +134,7 @@ static void attention_plans(Rng& rng, bool prefill) {
       CHECK(rc2 == CSA_OK || rc2 == CSA_ERR_WORKSPACE, "rc2 %d", rc2);
       if (rc2 == CSA_OK) {
         const AttnParams& b = g_stub.attn;
-        const uint64_t pb = (uint64_t)b.n_splits * T * H * (D + kPartPad) * 4;
+        const uint64_t pb = (uint64_t)b.n_splits * T * H * part_row_bytes(D);
         CHECK(b.n_splits == 1 ? half == 0 || true : pb <= half, "coarser partials %llu > %zu", (unsigned long long)pb,
               half);
         CHECK((int64_t)b.n_splits * b.per_split >= need_slots && b.per_split <= kAttnMaxSlots, "coarser split");
@@ -148,10 +148,10 @@ static void attention_plans(Rng& rng, bool prefill) {
       // the fewest splits the planner can use: the selected slots may be
       // padded by up to a tile
       const int64_t plan_slots = max_keys + kAttnTile - 1;
-      const uint64_t min_part = (uint64_t)((plan_slots + kAttnMaxSlots - 1) / kAttnMaxSlots) * T * H * (D + kPartPad) * 4;
+      const uint64_t min_part = (uint64_t)((plan_slots + kAttnMaxSlots - 1) / kAttnMaxSlots) * T * H * part_row_bytes(D);
       if (rc3 == CSA_OK) {
         const AttnParams& c = g_stub.attn;
-        CHECK(c.n_splits == 1 || (uint64_t)c.n_splits * T * H * (D + kPartPad) * 4 <= CSA_NOALLOC_SCRATCH_BYTES,
+        CHECK(c.n_splits == 1 || (uint64_t)c.n_splits * T * H * part_row_bytes(D) <= CSA_NOALLOC_SCRATCH_BYTES,
               "no-alloc partials beyond the scratch");
       } else {
         CHECK(rc3 == CSA_ERR_TOO_LARGE && min_part > CSA_NOALLOC_SCRATCH_BYTES,

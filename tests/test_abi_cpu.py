@@ -68,10 +68,10 @@ def test_workspace_sizes(lib):
     assert csa.csa_index_topk_workspace_size(64, 2048, 512) == 0
     # many queries: one workgroup per (query, 32 heads), no split
     assert csa.csa_attn_workspace_size(64, 128, 448, 64, 640) == 0
-    # one query: split over workgroups, partials of 512 + 2 floats per head
-    # padded to 516 (16-byte rows)
+    # one query: split over workgroups, a partial row per head of 512 BF16
+    # values plus (M, L) as floats, padded to 1040 bytes
     ws = csa.csa_attn_workspace_size(1, 128, 448, 64, 640)
-    assert ws > 0 and ws % (128 * 516 * 4) == 0
+    assert ws > 0 and ws % (128 * 1040) == 0
     # key ranges beyond 128 splits of 2048 slots are not supported
     assert lib.csa_attn_workspace_size(1, 128, 448, 64, 128 * 2048) == csa.CSA_WORKSPACE_UNSUPPORTED
     assert lib.csa_attn_workspace_size(1, 128, 100, 64, 640) == csa.CSA_WORKSPACE_UNSUPPORTED   # unsupported dims

@@ -80,7 +80,7 @@ def test_noalloc_hca_long_context_then_tiny():
 def test_noalloc_rejects_partials_beyond_the_scratch():
     # 64 HCA queries whose page-table rows span 2048 entries: with the
     # 128-slot window every key range needs at least two splits, and the
-    # minimum partial results (2 x 64 x 128 x 516 floats, 34 MB) exceed the
+    # minimum partial results (2 x 64 x 128 rows of 1040 bytes, 17 MB) exceed the
     # 16 MiB scratch, so the call is refused on the host before any launch.
     # (Every page-table entry is the one zero page and nothing is stored, so
     # even a launch would read in bounds.)
