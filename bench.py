@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--mxfp4", action="store_true",
                     help="indexer on MXFP4 inputs (csa_index_scores_mxfp4) instead of E4M3")
     ap.add_argument("--fused-topk", action="store_true",
-                    help="steps 1+2 as one call (csa_index_topk, decode only)")
+                    help="steps 1+2 as one call (csa_index_topk: the scores stay on chip)")
     ap.add_argument("--topk-in-attn", action="store_true",
                     help="steps 2-4 as one call (csa_topk_decode_attn: the attention kernel selects the top-k; "
                          "decode rows up to 8192 entries)")

@@ -51,7 +51,7 @@ def make_path(d, csa=None, inv_rope_theta=0.0, mxfp4=False, fused_topk=False, to
     """DecodePath (decode workloads) or PrefillPath (prefill chunk); a
     nonzero inv_rope_theta turns on the inverse-RoPE epilogue; mxfp4 feeds
     the indexer the MXFP4 copy of its inputs; fused_topk runs steps 1+2 as
-    one call, topk_in_attn steps 2-4 (decode)."""
+    one call (decode and prefill), topk_in_attn steps 2-4 (decode)."""
     if csa is None:
         import sparse_compressed_attention_amd as csa  # noqa: PLC0415
     s = d.spec
@@ -68,4 +68,5 @@ def make_path(d, csa=None, inv_rope_theta=0.0, mxfp4=False, fused_topk=False, to
                               topk_in_attn=topk_in_attn, **idx)
     return csa.PrefillPath(cache=cache, seq=0, q=d.q, q_pos=d.q_pos, sink=d.sink, softmax_scale=s.sigma, k=s.k,
                            W=s.W, swa_nope=d.swa_nope, swa_rope=d.swa_rope, swa_scale=d.swa_scale,
-                           swa_first_pos=d.swa_first_pos, inv_rope_theta=inv_rope_theta, **idx)
+                           swa_first_pos=d.swa_first_pos, inv_rope_theta=inv_rope_theta, fused_topk=fused_topk,
+                           **idx)

@@ -195,16 +195,23 @@ int csa_topk(const float* scores, int64_t ld_scores, const int32_t* n_visible,
 
 /* ---- Steps 1+2 fused ([Audit] B2: weighted-ReLU MQA logits and a top-k
  * with a wave-local reduction and no global lock) --------------------------
- * The result of csa_index_scores followed by csa_topk (same arguments, same
- * selection rule, bit-identical indices), without writing the scores: one
- * workgroup per (row, chunk of 2048, 4096 or 8192 entries) keeps its
- * chunk's scores in LDS and selects the chunk's top-k there; rows longer
- * than one chunk are finished by the top-k merge over the chunks'
- * candidates.  Outputs: topk_idx [T][k] (ascending, -1 padding) and
- * n_visible [T].  E4M3 operands only.
+ * The result of csa_index_scores followed by csa_topk with ld_scores =
+ * max_pages * page_size (same selection rule, bit-identical indices),
+ * without writing the scores.  Two plans:
+ *   - one sequence (B == 1), T >= 16, k <= 1024, max_pages * page_size <=
+ *     65536 (a prefill chunk): workgroups of 8 queries share each key tile
+ *     and every query keeps a candidate buffer on chip (entries above a
+ *     running threshold, cut back to about k when full); the key range is
+ *     split over workgroups when there are fewer query blocks than CUs;
+ *   - otherwise one workgroup per (row, chunk of 2048, 4096 or 8192
+ *     entries) keeps its chunk's scores in LDS and selects the chunk's
+ *     top-k there.
+ * Rows whose range was split are finished by the top-k merge over the
+ * parts' candidates.  Outputs: topk_idx [T][k] (ascending, -1 padding) and
+ * n_visible [T] (clamped to max_pages * page_size).  E4M3 operands only.
  * Workspace: csa_index_topk_workspace_size(T, max_pages * page_size, k)
- * bytes (0 when a row fits one chunk; NULL is then allowed;
- * CSA_WORKSPACE_UNSUPPORTED for arguments csa_index_topk rejects).
+ * bytes, enough for either plan (0 when no row is split; NULL is then
+ * allowed; CSA_WORKSPACE_UNSUPPORTED for arguments csa_index_topk rejects).
  * Supported: 1 <= k <= 2048 and (max_pages * page_size) / 8192 chunks of k
  * candidates within the merge's 16384 (CSA_ERR_UNSUPPORTED otherwise).
  * Errors: CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE,

@@ -514,6 +514,18 @@ class _Path:
             _ptr(self.q_idx), float(self.q_idx_scale), _ptr(self.w), _ptr(self.k_idx), float(self.k_idx_scale),
             *tail, DQ, int(self.cache.ratio_m), _ptr(self.scores), self.ld, _ptr(self.n_vis)))
 
+    def _index_topk_stage(self):
+        """Steps 1+2 as one call (csa_index_topk, E4M3 operands)."""
+        T, H_I, D_I = self.q_idx.shape
+        P, ps, _ = self.k_idx.shape
+        pt = self.cache.page_table
+        tw = 0 if self.topk_ws is None else self.topk_ws.numel()
+        return ("csa_index_topk", (
+            _ptr(self.q_idx), float(self.q_idx_scale), _ptr(self.w), _ptr(self.k_idx), float(self.k_idx_scale),
+            _ptr(pt), _ptr(self.cache.n_comp), P, ps, pt.shape[1], pt.shape[0], _ptr(self.q_pos), _ptr(self.q_seq),
+            T, H_I, D_I, int(self.cache.ratio_m), self.k, _ptr(self.topk), _ptr(self.n_vis), _ptr(self.topk_ws),
+            tw))
+
     def run_stage(self, i: int, stream=None):
         fn, name, args = self._stages[i]
         rc = fn(*args, _stream(stream))
@@ -594,14 +606,7 @@ class DecodePath(_Path):
             _need(self.w, "w", _F32, 2)
             tw = 0 if self.topk_ws is None else self.topk_ws.numel()
             if self.fused_topk:
-                T, H_I, D_I = self.q_idx.shape
-                P, ps, _ = self.k_idx.shape
-                pt = self.cache.page_table
-                plan.append(("csa_index_topk", (
-                    _ptr(self.q_idx), float(self.q_idx_scale), _ptr(self.w), _ptr(self.k_idx),
-                    float(self.k_idx_scale), _ptr(pt), _ptr(self.cache.n_comp), P, ps, pt.shape[1], pt.shape[0],
-                    _ptr(self.q_pos), _ptr(self.q_seq), T, H_I, D_I, int(self.cache.ratio_m), self.k,
-                    _ptr(self.topk), _ptr(self.n_vis), _ptr(self.topk_ws), tw)))
+                plan.append(self._index_topk_stage())
             elif self.topk_in_attn:
                 plan.append(self._index_stage())
             else:
@@ -629,16 +634,16 @@ class DecodePath(_Path):
 
 class PrefillPath(_Path):
     """One CSA prefill chunk (T queries of one sequence) with buffers
-    allocated once."""
-
-    stage_names = ("index_scores", "topk", "prefill_attn")
+    allocated once.  fused_topk runs steps 1+2 as one call that keeps the
+    scores on chip (E4M3 indexer inputs)."""
 
     def __init__(self, *, cache: LatentCache, seq, q, q_pos, sink, softmax_scale, k, W, swa_nope, swa_rope,
                  swa_scale, swa_first_pos, q_idx, q_idx_scale, w, k_idx, k_idx_scale, inv_rope_theta=0.0,
-                 q_idx_sc=None, k_idx_sc=None):
+                 q_idx_sc=None, k_idx_sc=None, fused_topk=False):
         dev = q.device
         self.inv_rope_theta = float(inv_rope_theta)
         self.q_idx_sc, self.k_idx_sc = q_idx_sc, k_idx_sc   # both given: MXFP4 indexer inputs
+        self.fused_topk = bool(fused_topk) and q_idx_sc is None
         self.cache, self.seq, self.q, self.q_pos, self.sink = cache, int(seq), q, q_pos, sink
         self.softmax_scale, self.k, self.W = float(softmax_scale), int(k), int(W)
         self.swa_nope, self.swa_rope, self.swa_scale, self.swa_first_pos = swa_nope, swa_rope, swa_scale, swa_first_pos
@@ -648,10 +653,16 @@ class PrefillPath(_Path):
         self.q_seq = torch.full((T,), self.seq, dtype=torch.int32, device=dev)
         max_entries = cache.page_table.shape[1] * cache.nope.shape[1]
         self.ld = max(16, (max_entries + 15) // 16 * 16)
-        self.scores = torch.empty((T, self.ld), dtype=torch.float32, device=dev)
         self.n_vis = torch.empty((T,), dtype=torch.int32, device=dev)
         self.topk = torch.empty((T, self.k), dtype=torch.int32, device=dev)
-        tw = csa_topk_workspace_size(T, self.ld, self.k)
+        if self.fused_topk:
+            self.scores = None
+            tw = csa_index_topk_workspace_size(T, max_entries, self.k)
+            self.stage_names = ("index_topk", "prefill_attn")
+        else:
+            self.scores = torch.empty((T, self.ld), dtype=torch.float32, device=dev)
+            tw = csa_topk_workspace_size(T, self.ld, self.k)
+            self.stage_names = ("index_scores", "topk", "prefill_attn")
         self.topk_ws = torch.empty((max(tw, 16),), dtype=torch.uint8, device=dev) if tw else None
         self.out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -673,10 +684,13 @@ class PrefillPath(_Path):
         _need(self.swa_rope, "swa_rope", _B16, 2)
         tw = 0 if self.topk_ws is None else self.topk_ws.numel()
         aw = 0 if self.attn_ws is None else self.attn_ws.numel()
-        return [
-            self._index_stage(),
-            ("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), T, self.k, _ptr(self.topk),
-                          _ptr(self.topk_ws), tw)),
+        if self.fused_topk:
+            steps = [self._index_topk_stage()]
+        else:
+            steps = [self._index_stage(),
+                     ("csa_topk", (_ptr(self.scores), self.ld, _ptr(self.n_vis), T, self.k, _ptr(self.topk),
+                                   _ptr(self.topk_ws), tw))]
+        return steps + [
             ("csa_prefill_attn", (
                 _ptr(self.q), self.q.stride(0), ctypes.byref(self._cc), self.seq, _ptr(self.topk), self.k,
                 _ptr(self.swa_nope), _ptr(self.swa_rope), float(self.swa_scale), int(self.swa_first_pos),

@@ -66,6 +66,23 @@ TopkPlan plan_index_topk(int32_t T, int64_t span, int32_t k) {
   return pl;
 }
 
+// Many queries of one sequence (B == 1, T >= 16, k <= 1024, at most 65536
+// entries): workgroups of 8 queries sharing each key tile, the key range cut
+// into n parts of at least 1024 entries when there are fewer query blocks
+// than CUs; candidates of n parts x k per row go to the merge.
+TopkPlan plan_index_topk_prefill(int32_t T, int64_t span, int32_t k) {
+  TopkPlan pl;
+  if (T < 16 || k < 1 || k > kIndexTopkPrefillMaxK || span < 1 || span > kIndexTopkPrefillMaxSpan) return pl;
+  const int64_t n_qb = ceil_div(T, kIndexTopkPrefillQ);
+  const int64_t n = std::max<int64_t>(
+      1, std::min<int64_t>({ceil_div(256, n_qb), ceil_div(span, 256) / 4, (int64_t)(kTopkMaxCand / k)}));
+  pl.chunk = (int)ceil_div(span, n);
+  pl.n_chunks = (int)n;
+  pl.ws_bytes = n > 1 ? (size_t)T * (size_t)n * (size_t)k * 8u : 0;
+  pl.ok = true;
+  return pl;
+}
+
 // ---- attention split of the key range over workgroups ---------------------
 constexpr int kTargetBlocks = 256;   // one workgroup per CU on MI355X
 struct AttnPlan {
@@ -217,7 +234,10 @@ int csa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_idx_sc, const 
 size_t csa_index_topk_workspace_size(int32_t T, int64_t max_entries, int32_t k) {
   if (T < 1 || max_entries < 1 || k < 1 || k > kTopkMaxK) return CSA_WORKSPACE_UNSUPPORTED;
   const TopkPlan pl = plan_index_topk(T, max_entries, k);
-  return pl.ok ? pl.ws_bytes : CSA_WORKSPACE_UNSUPPORTED;
+  if (!pl.ok) return CSA_WORKSPACE_UNSUPPORTED;
+  // one sequence may take the many-query plan (B is not an argument here)
+  const TopkPlan pm = plan_index_topk_prefill(T, max_entries, k);
+  return pm.ok ? std::max(pl.ws_bytes, pm.ws_bytes) : pl.ws_bytes;
 }
 
 int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w, const uint8_t* k_idx, float k_idx_scale,
@@ -237,8 +257,10 @@ int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w, cons
   if (H_I < 1 || H_I > 64 || !(D_I == 32 || D_I == 64 || D_I == 96 || D_I == 128)) return CSA_ERR_UNSUPPORTED;
   if (k < 1 || k > kTopkMaxK) return CSA_ERR_UNSUPPORTED;
   const int64_t span = (int64_t)max_pages * page_size;
-  const TopkPlan pl = plan_index_topk(T, span, k);
-  if (!pl.ok) return CSA_ERR_UNSUPPORTED;
+  const TopkPlan pl0 = plan_index_topk(T, span, k);
+  if (!pl0.ok) return CSA_ERR_UNSUPPORTED;
+  const TopkPlan pm = B == 1 ? plan_index_topk_prefill(T, span, k) : TopkPlan();
+  const TopkPlan& pl = pm.ok ? pm : pl0;
   if (pl.n_chunks > 1 && (!workspace || !aligned16(workspace) || workspace_bytes < pl.ws_bytes))
     return CSA_ERR_WORKSPACE;
   if ((int64_t)T * pl.n_chunks >= ((int64_t)1 << 31)) return CSA_ERR_UNSUPPORTED;
@@ -270,6 +292,10 @@ int csa_index_topk(const uint8_t* q_idx, float q_idx_scale, const float* w, cons
     tp.cand_key = static_cast<uint32_t*>(workspace);
     tp.cand_idx = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + pl.ws_bytes / 2);
   }
+  // rows see at most the page table's entries (as csa_index_scores with
+  // ld_scores = max_pages * page_size)
+  p.ld = span;
+  if (pm.ok) return launch_status(launch_index_topk_prefill(p, tp, (hipStream_t)stream));
   return launch_status(launch_index_topk(p, tp, (hipStream_t)stream));
 }
 

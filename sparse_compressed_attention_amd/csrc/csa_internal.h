@@ -48,6 +48,14 @@ hipError_t launch_topk_merge(const TopkParams& p, hipStream_t stream);
 // LDS; one workgroup per (row, chunk of `chunk` entries) selects the chunk's
 // top-k, then the merge (when a row has several chunks)
 hipError_t launch_index_topk(const IndexParams& ip, const TopkParams& tp, hipStream_t stream);
+// fused indexer + top-k for many queries of one sequence (ip.B == 1, ip.ld =
+// the key range, at most 65536 entries): workgroups of kIndexTopkPrefillQ
+// queries share each key tile, each query keeps a candidate buffer in LDS;
+// tp.n_chunks parts of the key range per query block, then the merge
+hipError_t launch_index_topk_prefill(const IndexParams& ip, const TopkParams& tp, hipStream_t stream);
+constexpr int kIndexTopkPrefillQ = 8;
+constexpr int kIndexTopkPrefillMaxK = 1024;
+constexpr int64_t kIndexTopkPrefillMaxSpan = 65536;
 constexpr int kTopkMaxChunk = 16384;
 constexpr int kTopkMaxCand = 16384;
 constexpr int kTopkMaxK = 2048;

@@ -244,6 +244,27 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   }
 }
 
+// Minimum / maximum over the wave: rotations within each row of 16 lanes
+// (DPP row_ror 8, 4, 2, 1), then the four rows through readlane.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return min(a, b);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return max(a, b);
+}
+
 // ---- many queries of one sequence (prefill) -----------------------------
 // All queries scan the same compressed keys, so a workgroup of kMqQ waves
 // takes kMqQ queries (one per wave) and walks the whole key range in chunks
@@ -257,7 +278,6 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
 constexpr int kMqQ = 8;
 constexpr int kMqGroups = 16;
 constexpr int kMqChunk = 16 * kMqGroups;
-constexpr int kMqGpw = kMqGroups / kMqQ;    // groups loaded per wave per chunk
 static_assert(kMqGroups % kMqQ == 0, "groups split evenly over the waves");
 static_assert(kMqGroups % 4 == 0, "groups are reduced four at a time");
 
@@ -265,13 +285,38 @@ static_assert(kMqGroups % 4 == 0, "groups are reduced four at a time");
 // kFp4 (MXFP4 operands, as in the one-query kernel): a lane's LDS slot of a
 // group holds its 16 code bytes in dwords 0-3 and its block's scale byte in
 // dword 4; the scaled MFMA reads only dwords 0-3 of an FP4 operand.
-template <bool kFp4>
-__global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexParams p, int n_split) {
+//
+// kQ queries (waves) per workgroup.  kFused: the scores never leave the
+// chip.  Every wave keeps a candidate buffer of (key, entry) pairs in LDS, in
+// entry order, and a threshold: an entry goes in only if its
+// order-preserving key is above the threshold (later entries are higher in
+// index, so one tied with the threshold ranks below every kept one).  When a
+// buffer could overflow in the next chunk, the waves cut their buffers to a
+// little more than k entries by a threshold found by bisection over key
+// values (exactly k where ties decide), which becomes the new insertion
+// threshold.  After the last chunk each buffer is cut to the exact top k of
+// the workgroup's key range, written as the row's answer (one range) or as
+// candidates for the top-k merge.  The scores come from the same code as in
+// the scores kernel, so the selection is bit-identical to csa_index_scores +
+// csa_topk.
+constexpr int kFtMqCap = 1792;   // candidate slots per wave (8 waves: 84 KB of LDS)
+constexpr int kFtMqMaxK = 1024;   // largest k: a cut leaves room for at least one chunk
+static_assert(kFtMqCap - kMqChunk >= kFtMqMaxK, "a buffer cut to k has room for a chunk");
+template <bool kFp4, int kQ, bool kFused>
+__global__ __launch_bounds__(64 * kQ, kFused ? 1 : 2) void index_scores_mq_kernel(IndexParams p, TopkParams tp,
+                                                                                int n_split) {
+  static_assert(!kFused || !kFp4, "fused indexer + top-k: E4M3 operands");
+  constexpr int kMqGpw = kMqGroups / kQ;    // groups loaded per wave per chunk
+  static_assert(kMqGroups % kQ == 0 && kMqGpw >= 1, "groups split evenly over the waves");
   __shared__ __attribute__((aligned(16))) v8i ks[2][kMqGroups * 64];
-  __shared__ uint32_t okw[2][kMqQ];
-  // workgroup = (query block, part of the key range): n_split parts so that
-  // a CU runs two workgroups (four waves per SIMD) and the MFMAs of one wave
-  // overlap the weighted-ReLU work of another
+  __shared__ uint32_t okw[2][kQ];
+  // fused: each wave's candidate keys and entries, and whether its buffer
+  // needs a cut before the next chunk
+  __shared__ uint32_t fck[kFused ? kQ : 1][kFused ? kFtMqCap : 1];
+  __shared__ uint16_t fci[kFused ? kQ : 1][kFused ? kFtMqCap : 1];
+  __shared__ int fneed[2][kQ];
+  // workgroup = (query block, part of the key range): n_split parts when
+  // the query blocks alone would leave CUs idle
   const int qb = blockIdx.x / n_split;
   const int split = blockIdx.x - qb * n_split;
   const int lane = threadIdx.x & 63;
@@ -279,7 +324,7 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   const int g = lane >> 4;
   const int r = lane & 15;
   const bool dim_ok = 32 * g < p.D_I;
-  const int t = qb * kMqQ + wave;
+  const int t = qb * kQ + wave;
   const bool q_ok = t < p.T;
 
   // ---- this wave's query operand and weights (layout as in the
@@ -313,8 +358,8 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   const int nc = p.n_comp[0];
   int nv_max = 0, nv_own = 0;
 #pragma unroll
-  for (int w = 0; w < kMqQ; ++w) {
-    const int tw = qb * kMqQ + w;
+  for (int w = 0; w < kQ; ++w) {
+    const int tw = qb * kQ + w;
     int nv = 0;
     if (tw < p.T) {
       const int pos = p.q_pos[tw];
@@ -329,7 +374,118 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   const int per = (n_all + n_split - 1) / n_split;
   const int c_begin = split * per;
   const int n_ch = min(n_all, c_begin + per);   // chunks [c_begin, n_ch) of this workgroup
-  if (c_begin >= n_ch) return;                  // uniform over the workgroup
+
+  // ---- fused: this wave's candidate buffer (wave-local; the wave's LDS
+  // operations complete in order, so a wait for them is its only fence)
+  uint32_t* bk = fck[kFused ? wave : 0];
+  uint16_t* bi = fci[kFused ? wave : 0];
+  int fcnt = 0;           // candidates in the buffer (ascending entry order)
+  bool full = false;      // a cut has happened: only keys above ftau go in
+  uint32_t ftau = 0;
+  auto wave_sync = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+  };
+  auto lanes_below = [&](uint64_t m) -> int {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+  };
+  // Cuts the buffer (fcnt > U >= K >= 1) to the entries above a threshold
+  // thr that keeps between K and U of them, or, when ties leave no such
+  // threshold (and always when U == K), to exactly its top K: the keys above
+  // thr plus the first need_eq keys equal to it.  Either way every dropped
+  // entry, and every later entry whose key is not above thr, has at least K
+  // kept entries ranked above it, so thr becomes the insertion threshold.
+  // thr comes from a bisection over key values; each probe counts the keys
+  // above it with one compare and one ballot popcount per 64 slots (keys
+  // and entries are read into registers once, lane l holding slots 64 q + l).
+  auto shrink = [&](int K, int U) __attribute__((always_inline)) {
+    constexpr int kR = kFtMqCap / 64;
+    uint32_t kr[kR], ir[kR];
+    uint32_t vmin = 0xffffffffu, vmax = 0u;
+#pragma unroll
+    for (int q = 0; q < kR; ++q) {
+      const bool v = 64 * q + lane < fcnt;
+      kr[q] = v ? bk[64 * q + lane] : 0u;   // empty slots: key 0, above no probe
+      ir[q] = v ? bi[64 * q + lane] : 0u;
+      vmin = v ? min(vmin, kr[q]) : vmin;
+      vmax = v ? max(vmax, kr[q]) : vmax;
+    }
+    vmin = wave_min_u32(vmin);
+    vmax = wave_max_u32(vmax);
+    auto count_above = [&](uint32_t x) {
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < kR; ++q) n += __builtin_popcountll(__ballot(kr[q] > x));
+      return n;
+    };
+    // count_above(lo) >= K > count_above(hi)
+    int64_t lo = (int64_t)vmin - 1, hi = vmax;
+    int c_lo = fcnt, c_hi = 0;
+    while (c_lo > U && hi - lo > 1) {
+      const uint32_t mid = (uint32_t)(lo + ((hi - lo) >> 1));
+      const int c = count_above(mid);
+      if (c >= K) {
+        lo = mid;
+        c_lo = c;
+      } else {
+        hi = mid;
+        c_hi = c;
+      }
+    }
+    uint32_t thr;
+    int need_eq = 0;
+    if (c_lo <= U) {
+      thr = (uint32_t)lo;         // lo >= 0 here: it moved at least once
+    } else {
+      thr = (uint32_t)hi;         // hi == lo + 1: the keys equal to hi decide
+      need_eq = K - c_hi;
+    }
+    // ordered compaction in place (outputs never pass inputs, all of which
+    // are in registers)
+    int n_out = 0, eq_seen = 0;
+#pragma unroll
+    for (int q = 0; q < kR; ++q) {
+      const bool valid = 64 * q + lane < fcnt;
+      const bool eq = valid && kr[q] == thr;
+      const uint64_t eqb = __ballot(eq);
+      const bool take = (valid && kr[q] > thr) || (eq && eq_seen + lanes_below(eqb) < need_eq);
+      const uint64_t tb = __ballot(take);
+      if (take) {
+        const int pos = n_out + lanes_below(tb);
+        bk[pos] = kr[q];
+        bi[pos] = (uint16_t)ir[q];
+      }
+      n_out += __builtin_popcountll(tb);
+      eq_seen += __builtin_popcountll(eqb);
+    }
+    fcnt = n_out;
+    ftau = thr;
+    full = true;
+    wave_sync();
+  };
+  // the row's answer (one key range) or its candidates for the merge:
+  // min(k, fcnt) entries in ascending order, then padding
+  auto emit = [&]() {
+    if (fcnt > tp.k) shrink(tp.k, tp.k);
+    wave_sync();
+    if (n_split == 1) {
+      int32_t* o = tp.out + (size_t)t * tp.k;
+      for (int j = lane; j < tp.k; j += 64) o[j] = j < fcnt ? (int32_t)bi[j] : -1;
+    } else {
+      const size_t base = ((size_t)t * n_split + split) * tp.k;
+      for (int j = lane; j < tp.k; j += 64) {
+        tp.cand_key[base + j] = j < fcnt ? bk[j] : 0u;
+        tp.cand_idx[base + j] = j < fcnt ? (int32_t)bi[j] : -1;
+      }
+    }
+  };
+  if (c_begin >= n_ch) {                        // uniform over the workgroup
+    if constexpr (kFused) {
+      if (q_ok) emit();
+    }
+    return;
+  }
 
   // page id of group (4 w + j) of chunk c, fetched by lane j (< kMqGpw)
   auto load_page = [&](int c) -> int {
@@ -382,7 +538,7 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
   store_keys(0, kl, okbits);
   __syncthreads();
 
-  float* out = p.scores + (size_t)t * p.ld;
+  float* out = kFused ? nullptr : p.scores + (size_t)t * p.ld;
   auto mfmas = [&](const v8i& k, v4f (&acc)[4]) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
@@ -407,12 +563,13 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
     if (q_ok && e0 < nv_own) {
       uint32_t ok_mask = 0;
 #pragma unroll
-      for (int w = 0; w < kMqQ; ++w) ok_mask |= okw[b][w];
+      for (int w = 0; w < kQ; ++w) ok_mask |= okw[b][w];
       const int e_end = min(nv_own, e0 + kMqChunk);
       // MFMAs of group u + 1 before the weighted ReLU of group u; one
       // reduce-scatter per four groups (as in the one-query kernel)
       v4f acc[2][4];
       float xg[4];
+      float sq[kMqGroups / 4];   // fused: entry e0 + 64 i + lane of the chunk
       v8i kb = ks[b][lane];
       mfmas(kb, acc[0]);
 #pragma unroll
@@ -425,13 +582,58 @@ __global__ __launch_bounds__(64 * kMqQ, 2) void index_scores_mq_kernel(IndexPara
         if ((u & 3) == 3) {
           const float tot = reduce4_scatter(xg[0], xg[1], xg[2], xg[3]);
           const int ug = u - 3 + g;
-          const int e = e0 + 16 * ug + r;
-          if (e < e_end) out[e] = ((ok_mask >> ug) & 1u) ? tot : -__builtin_inff();
+          const float v = ((ok_mask >> ug) & 1u) ? tot : -__builtin_inff();
+          if constexpr (kFused) {
+            sq[u >> 2] = v;
+          } else {
+            const int e = e0 + 16 * ug + r;
+            if (e < e_end) out[e] = v;
+          }
+        }
+      }
+      if constexpr (kFused) {
+        // lane l holds entry e0 + 64 i + l of block i: ballots in lane order
+        // keep the buffer in entry order
+        // (room for the whole chunk: fcnt <= kFtMqCap - kMqChunk here)
+        uint32_t key[kMqGroups / 4];
+        uint64_t bal[kMqGroups / 4];
+#pragma unroll
+        for (int i = 0; i < kMqGroups / 4; ++i) {
+          key[i] = float_order_key(sq[i]);
+          bal[i] = __ballot(e0 + 64 * i + lane < e_end && (!full || key[i] > ftau));
+        }
+#pragma unroll
+        for (int i = 0; i < kMqGroups / 4; ++i) {
+          if ((bal[i] >> lane) & 1u) {
+            const int pos = fcnt + lanes_below(bal[i]);
+            bk[pos] = key[i];
+            bi[pos] = (uint16_t)(e0 + 64 * i + lane);
+          }
+          fcnt += __builtin_popcountll(bal[i]);
         }
       }
     }
     if (more) store_keys(b ^ 1, kl, okbits);
+    if constexpr (kFused) {
+      if (lane == 0) fneed[b][wave] = fcnt > kFtMqCap - kMqChunk;
+    }
     __syncthreads();
+    if constexpr (kFused) {
+      // when any wave's buffer could overflow in the next chunk, every wave
+      // above U cuts now: the cuts of the workgroup run side by side instead
+      // of one after another between the chunk barriers.  U a little above
+      // k lets the bisection stop early (measured on 2048 queries x 16384
+      // entries, k 512: 310 us with U = k + 128 and 1792 slots, 320 us with
+      // U halfway to the trigger and 1280 slots)
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < kQ; ++w) any |= fneed[b][w];
+      const int U = min(tp.k + 128, kFtMqCap - kMqChunk);
+      if (any && more && fcnt > U) shrink(tp.k, U);
+    }
+  }
+  if constexpr (kFused) {
+    if (q_ok) emit();
   }
 }
 
@@ -498,7 +700,7 @@ __global__ __launch_bounds__(64 * kFtWaves, 1) void index_topk_kernel(IndexParam
   }
   int nv = 0;
   if (seq_ok && pos >= 0) nv = min(pos / p.ratio_m, p.n_comp[seq]);
-  nv = max(0, nv);
+  nv = max(0, (int)min<int64_t>(nv, p.ld));     // the page table's entries at most
   if (chunk == 0 && threadIdx.x == 0) p.n_visible[t] = nv;
   const int n = max(0, min(kChunk, nv - c0));   // visible entries of this chunk (uniform)
 
@@ -624,18 +826,33 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
     const int64_t span_ch = std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
     // about two workgroups per CU (256 CUs), parts of at least 4 chunks
     const int n_split = (int)std::max<int64_t>(1, std::min<int64_t>((512 + n_qb - 1) / n_qb, span_ch / 4));
+    const TopkParams none{};
     if (p.fp4)
-      hipLaunchKernelGGL(index_scores_mq_kernel<true>, dim3((unsigned)(n_qb * n_split)), dim3(64 * kMqQ), 0, stream,
-                         p, n_split);
+      hipLaunchKernelGGL((index_scores_mq_kernel<true, kMqQ, false>), dim3((unsigned)(n_qb * n_split)),
+                         dim3(64 * kMqQ), 0, stream, p, none, n_split);
     else
-      hipLaunchKernelGGL(index_scores_mq_kernel<false>, dim3((unsigned)(n_qb * n_split)), dim3(64 * kMqQ), 0, stream,
-                         p, n_split);
+      hipLaunchKernelGGL((index_scores_mq_kernel<false, kMqQ, false>), dim3((unsigned)(n_qb * n_split)),
+                         dim3(64 * kMqQ), 0, stream, p, none, n_split);
     return hipPeekAtLastError();
   }
   // MXFP4 operands: twice the groups per wave (a key row is half as long, so
   // the same bytes in flight)
   if (p.fp4) return launch_decode<4, 8, 4, true, true>(p, span, stream);
   return launch_decode<4, 4, 4, true, false>(p, span, stream);
+}
+
+hipError_t launch_index_topk_prefill(const IndexParams& p, const TopkParams& tp, hipStream_t stream) {
+  static_assert(kFtMqMaxK == kIndexTopkPrefillMaxK, "candidate buffer sized for the largest k");
+  if (p.B != 1 || p.T < 1 || tp.k < 1 || tp.k > kFtMqMaxK || tp.n_chunks < 1 || p.ld > kIndexTopkPrefillMaxSpan)
+    return hipErrorInvalidValue;
+  const int64_t n_qb = (p.T + kIndexTopkPrefillQ - 1) / kIndexTopkPrefillQ;
+  const int n_split = tp.n_chunks;
+  if (n_qb * n_split >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((index_scores_mq_kernel<false, kIndexTopkPrefillQ, true>), dim3((unsigned)(n_qb * n_split)),
+                     dim3(64 * kIndexTopkPrefillQ), 0, stream, p, tp, n_split);
+  hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess || n_split == 1) return e;
+  return launch_topk_merge(tp, stream);
 }
 
 hipError_t launch_index_topk(const IndexParams& p_in, const TopkParams& tp_in, hipStream_t stream) {

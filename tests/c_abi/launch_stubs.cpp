@@ -29,6 +29,13 @@ hipError_t launch_index_topk(const IndexParams& ip, const TopkParams& tp, hipStr
   ++g_stub.n_index_topk;
   return hipSuccess;
 }
+hipError_t launch_index_topk_prefill(const IndexParams& ip, const TopkParams& tp, hipStream_t) {
+  g_stub.index = ip;
+  g_stub.topk = tp;
+  ++g_stub.n_index_topk;
+  ++g_stub.n_index_topk_prefill;
+  return hipSuccess;
+}
 hipError_t launch_attn(const AttnParams& p, hipStream_t) {
   g_stub.attn = p;
   ++g_stub.n_attn;

@@ -9,7 +9,7 @@ struct StubLog {
   IndexParams index{};
   TopkParams topk{};
   AttnParams attn{};
-  int n_index = 0, n_topk = 0, n_index_topk = 0, n_attn = 0;
+  int n_index = 0, n_topk = 0, n_index_topk = 0, n_index_topk_prefill = 0, n_attn = 0;
 };
 extern StubLog g_stub;
 

@@ -213,11 +213,14 @@ static void index_plans(Rng& rng) {
       const IndexParams& p = g_stub.index;
       CHECK(p.T == T && p.ld == ld && p.H_I == HI && p.D_I == DI && p.qk_scale == 0.125f, "index params");
     }
-    // fused indexer + top-k
-    const int k = (int)rng.range(1, 2100);
-    const size_t ws = csa_index_topk_workspace_size(T, (int64_t)maxp * ps, k);
+    // fused indexer + top-k (one sequence: possibly the many-query plan)
+    const int k = (int)(rng.range(0, 1) ? rng.range(1, 2100) : rng.range(1, 1100));
+    const int B = rng.range(0, 1) ? 1 : 3;
+    const int64_t span = (int64_t)maxp * ps;
+    const size_t ws = csa_index_topk_workspace_size(T, span, k);
+    const int np0 = g_stub.n_index_topk_prefill;
     const int rc2 = csa_index_topk((const uint8_t*)dev(40), 0.5f, (const float*)dev(41), (const uint8_t*)dev(42), 0.25f,
-                                   (const int32_t*)dev(43), (const int32_t*)dev(44), 1000, ps, maxp, 3,
+                                   (const int32_t*)dev(43), (const int32_t*)dev(44), 1000, ps, maxp, B,
                                    (const int32_t*)dev(45), nullptr, T, HI, DI, 4, k, (int32_t*)dev(48),
                                    (int32_t*)dev(47), ws && ws != CSA_WORKSPACE_UNSUPPORTED ? dev(49) : nullptr,
                                    ws == CSA_WORKSPACE_UNSUPPORTED ? 0 : ws, nullptr);
@@ -227,8 +230,13 @@ static void index_plans(Rng& rng) {
       CHECK(rc2 == CSA_OK || rc2 == CSA_ERR_UNSUPPORTED, "fused rc %d", rc2);
       if (rc2 == CSA_OK) {
         const TopkParams& t = g_stub.topk;
-        CHECK((int64_t)t.chunk * t.n_chunks >= (int64_t)maxp * ps, "fused chunks");
+        const bool many = g_stub.n_index_topk_prefill != np0;
+        CHECK(many == (B == 1 && T >= 16 && k <= kIndexTopkPrefillMaxK && span <= kIndexTopkPrefillMaxSpan),
+              "plan choice B %d T %d k %d span %lld", B, T, k, (long long)span);
+        CHECK(g_stub.index.ld == span, "fused key range");
+        CHECK((int64_t)t.chunk * t.n_chunks >= span, "fused chunks");
         CHECK(t.n_chunks == 1 || (uint64_t)T * t.n_chunks * k * 8 <= ws, "fused candidates beyond the workspace");
+        CHECK((int64_t)t.n_chunks * k <= kTopkMaxCand || t.n_chunks == 1, "merge input beyond its capacity");
       }
     }
   }
@@ -274,6 +282,7 @@ int main() {
   topk_plans(rng);
   index_plans(rng);
   topk_attention_plans(rng);
+  CHECK(g_stub.n_index_topk_prefill > 0, "the many-query fused plan was never taken");
   printf("host ABI checks: %d failures (attention launches %d, top-k %d, indexer %d, fused %d)\n", g_fail,
          g_stub.n_attn, g_stub.n_topk, g_stub.n_index, g_stub.n_index_topk);
   return g_fail ? 1 : 0;

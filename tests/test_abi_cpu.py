@@ -65,7 +65,17 @@ def test_workspace_sizes(lib):
         csa.csa_topk_workspace_size(1, 1 << 22, 2048)
     assert lib.csa_topk_workspace_size(4, 8192, 4096) == csa.CSA_WORKSPACE_UNSUPPORTED   # k > 2048
     assert lib.csa_index_topk_workspace_size(64, 8192, 0) == csa.CSA_WORKSPACE_UNSUPPORTED
-    assert csa.csa_index_topk_workspace_size(64, 2048, 512) == 0
+    # rows of one chunk: no candidates leave the chip (fewer than 16 queries)
+    assert csa.csa_index_topk_workspace_size(8, 2048, 512) == 0
+    # 64 queries of one sequence (eight blocks of 8) may cut 2048 entries into
+    # 2 parts of 1024 with 512 candidates each; beyond 65536 entries or k > 1024
+    # only the one-query plan applies
+    assert csa.csa_index_topk_workspace_size(64, 2048, 512) == 64 * 2 * 512 * 8
+    assert csa.csa_index_topk_workspace_size(64, 2048, 1025) == 0
+    # 2048 queries over 16384 entries: the many-query plan needs none (256
+    # query blocks, no split), the one-query plan 8 chunks of 2048
+    assert csa.csa_index_topk_workspace_size(2048, 16384, 512) == 2048 * 8 * 512 * 8
+    assert csa.csa_index_topk_workspace_size(40, 15000, 512) == 40 * 14 * 512 * 8
     # many queries: one workgroup per (query, 32 heads), no split
     assert csa.csa_attn_workspace_size(64, 128, 448, 64, 640) == 0
     # one query: split over workgroups, a partial row per head of 512 BF16

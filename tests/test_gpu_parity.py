@@ -307,6 +307,98 @@ def test_fused_index_topk_equals_two_calls(case):
     say(f"  {case}: fused == two calls; exact top-k sets vs oracle {exact}")
 
 
+def _prefill_fused_case(case):
+    """Prefill workloads for the many-query fused indexer + top-k, and the
+    rows the oracle checks."""
+    if case == "c4":
+        return ci.make_config("c4"), [0, 1000, 2047]
+    if case == "ragged_T70":
+        spec = ci.Spec(name="prefill_small", kind="prefill", ctx_lens=[6000], T_prefill=70)
+        return ci.generate(spec, seed=181), [0, 33, 69]
+    if case == "T16":
+        spec = ci.Spec(name="prefill_t16", kind="prefill", ctx_lens=[9000], T_prefill=16, shuffle_pages=True)
+        return ci.generate(spec, seed=182), [0, 15]
+    if case == "split_merge":
+        # few query blocks and a long key range: the range is cut into parts
+        # whose candidates go through the merge
+        spec = ci.Spec(name="prefill_split", kind="prefill", ctx_lens=[60000], T_prefill=40, shuffle_pages=True)
+        return ci.generate(spec, seed=183), [0, 39]
+    if case == "k1024":
+        spec = ci.Spec(name="prefill_k1024", kind="prefill", ctx_lens=[20000], T_prefill=50, k=1024)
+        return ci.generate(spec, seed=184), [0, 49]
+    if case == "k_above_buffer":
+        # k beyond the per-query candidate buffer: the one-query fused kernel
+        spec = ci.Spec(name="prefill_k1500", kind="prefill", ctx_lens=[20000], T_prefill=24, k=1500)
+        return ci.generate(spec, seed=185), [0, 23]
+    if case == "tiny_dims":
+        spec = ci.Spec(name="prefill_tiny", kind="prefill", ctx_lens=[3000], T_prefill=45, H=8, D_nope=48,
+                       D_rope=16, H_I=4, D_I=32, k=16, W=32, page_size=16, shuffle_pages=True)
+        return ci.generate(spec, seed=186), [0, 44]
+    if case in ("all_tied", "five_values"):
+        # every key row a copy of one of n rows: scores tie exactly, so the
+        # selection leans on the lower-index rule across buffer cuts
+        spec = ci.Spec(name="prefill_ties", kind="prefill", ctx_lens=[16000], T_prefill=33)
+        wl = ci.generate(spec, seed=187)
+        n = 1 if case == "all_tied" else 5
+        rng = np.random.default_rng(188)
+        P_, ps, di = wl.k_idx.shape
+        rows = wl.k_idx.reshape(-1, di)
+        pick = rows[rng.integers(0, n, size=rows.shape[0]) if n > 1 else np.zeros(rows.shape[0], dtype=np.int64)]
+        return dataclasses.replace(wl, k_idx=pick.reshape(P_, ps, di).copy()), []
+    assert case == "poisoned"
+    # own and future blocks made the strongest keys: never selected
+    spec = ci.Spec(name="prefill_poisoned", kind="prefill", ctx_lens=[12000], T_prefill=64, shuffle_pages=True)
+    wl = ci.generate(spec, seed=189)
+    s = wl.spec
+    k_idx = wl.k_idx.copy()
+    nv_min = oracle.n_visible(int(wl.q_pos[0]), s.m, int(wl.n_comp[0]))
+    for c in range(nv_min, int(wl.n_comp[0])):
+        page = int(wl.page_table[0][c // s.page_size])
+        k_idx[page, c % s.page_size] = wl.q_idx[0][0]
+    return dataclasses.replace(wl, k_idx=k_idx), [0, 63]
+
+
+@pytest.mark.parametrize("case", ["ragged_T70", "T16", "split_merge", "k1024", "k_above_buffer", "tiny_dims",
+                                  "all_tied", "five_values", "poisoned", "c4"])
+def test_fused_index_topk_prefill_equals_two_calls(case):
+    # many queries of one sequence: workgroups of queries share each key
+    # tile and every query keeps a candidate buffer on chip; the indices are
+    # bit-identical to csa_index_scores + csa_topk (and gated against the
+    # oracle on sampled rows)
+    say(f"case fused prefill indexer + top-k {case}")
+    wl, qs = _prefill_fused_case(case)
+    d = to_device(wl, "cuda")
+    two = make_path(d)
+    fused = make_path(d, fused_topk=True)
+    assert fused.stage_names == ("index_topk", "prefill_attn")
+    two.run()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        fused.topk.fill_(-7)
+        fused.n_vis.fill_(-7)
+        fused.run()
+        torch.cuda.synchronize()
+        bad = (two.topk != fused.topk).any(dim=1).nonzero().flatten().tolist()
+        assert not bad, f"call {rep}: rows {bad[:8]} differ"
+        assert torch.equal(two.n_vis, fused.n_vis)
+        assert torch.equal(two.out.view(torch.int16), fused.out.view(torch.int16))
+    topk = fused.topk.cpu().numpy()
+    scores = two.scores.cpu().numpy()
+    n_vis = two.n_vis.cpu().numpy()
+    for t in range(0, wl.T, max(1, wl.T // 16)):
+        P.check_topk_exact_on_gpu_scores(topk[t], scores[t][:n_vis[t]], wl.spec.k)
+    if case == "all_tied":
+        for t in range(wl.T):
+            K = min(wl.spec.k, int(n_vis[t]))
+            assert (topk[t][:K] == np.arange(K)).all() and (topk[t][K:] == -1).all()
+    if case == "poisoned":
+        assert all((topk[t] < n_vis[t]).all() for t in range(wl.T))
+    exact = 0
+    for t in qs:
+        exact += P.check_topk_vs_oracle(topk[t], oracle.index_scores(wl, t), wl.spec.k)
+    say(f"  {case}: fused == two calls on {wl.T} rows; exact top-k sets vs oracle {exact}/{len(qs)}")
+
+
 # --------------------------------------------------------------- MXFP4 indexer
 @pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "prefill_small", "tiny_dims_wide",
                                   "heads40_dims64", "heads24_dims96_prefill"])
