@@ -132,12 +132,13 @@ def measured_peaks(torch, stream, reps=5):
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
-    blocks = 256 * 16
 
-    def copy():
+    def copy(blocks):
         if lib.csa_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, blocks, st):
             raise RuntimeError("csa_peak_copy failed")
-    t_copy = timed(copy)
+    # the fastest of three grid sizes (fewer, longer-lived workgroups leave
+    # part of the bandwidth unused on this part)
+    t_copy, blocks = min((timed(lambda b=b: copy(b)), b) for b in (256 * 16, 256 * 64, 256 * 256))
     if not torch.equal(src[:1024], dst[:1024]):
         raise RuntimeError("copy probe produced wrong bytes")
     del src, dst
@@ -150,7 +151,8 @@ def measured_peaks(torch, stream, reps=5):
     t_mfma = timed(mfma)
     flops = mblocks * 4 * iters * lib.csa_peak_mfma_chains() * 2 * 16 * 16 * 128
     return dict(copy_GBps=round(2 * nbytes / t_copy / 1e9, 1), fp8_mfma_TFLOPs=round(flops / t_mfma / 1e12, 1),
-                how=f"copy: {blocks} x 256 threads over 1 GiB -> 1 GiB, median of {reps}; MFMA: {mblocks} x 4 "
+                how=f"copy: {blocks} x 256 threads over 1 GiB -> 1 GiB (fastest of 4096, 16384, 65536 workgroups), "
+                    f"median of {reps}; MFMA: {mblocks} x 4 "
                     f"waves x {iters} x {lib.csa_peak_mfma_chains()} independent 16x16x128 FP8, median of {reps}")
 
 

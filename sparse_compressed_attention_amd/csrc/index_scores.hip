@@ -838,7 +838,10 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
   // MXFP4 operands: twice the groups per wave (a key row is half as long, so
   // the same bytes in flight)
   if (p.fp4) return launch_decode<4, 8, 4, true, true>(p, span, stream);
-  return launch_decode<4, 4, 4, true, false>(p, span, stream);
+  // 8 waves of 4 groups (512 entries per workgroup): 0.4 us faster at c2
+  // and 1.2 us at c3 than 4 waves (fewer workgroups to dispatch and fewer
+  // of them past a short row's end)
+  return launch_decode<8, 4, 4, true, false>(p, span, stream);
 }
 
 hipError_t launch_index_topk_prefill(const IndexParams& p, const TopkParams& tp, hipStream_t stream) {
