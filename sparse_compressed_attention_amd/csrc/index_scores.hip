@@ -824,7 +824,8 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
     p.n_chunks = (int)std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
     const int64_t n_qb = (p.T + kMqQ - 1) / kMqQ;
     const int64_t span_ch = std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
-    // about two workgroups per CU (256 CUs), parts of at least 4 chunks
+    // about 512 workgroups (at 152 registers a CU holds one at a time), parts
+    // of at least 4 chunks
     const int n_split = (int)std::max<int64_t>(1, std::min<int64_t>((512 + n_qb - 1) / n_qb, span_ch / 4));
     const TopkParams none{};
     if (p.fp4)
