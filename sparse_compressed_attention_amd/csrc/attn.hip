@@ -166,7 +166,7 @@ struct Block {
   int n_sel, sel_end, kv0, nkeys;   // slots: [0, n_sel) selected, [sel_end, sel_end + W) window
 };
 
-template <int DN, int DR, int DP, int HT, int ND>
+template <int DN, int DR, int DP, int HT, int ND, bool kProd>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, uint8_t* xs0, int32_t* desc,
                                           v4f* sx, v2i* pxh, v2i* pxb, int wave, const int32_t* sel) {
   using C = Cfg<DN, DR>;
@@ -324,13 +324,15 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   };
 
   const int n_tiles = (nkeys + kAttnTile - 1) / kAttnTile;
-  if (n_tiles > 0) {
-    prep_tile(0);
-    issue_quads(0, -1);
-  }
-  if (n_tiles > 1) {
-    prep_tile(1);
-    issue_quads(1, -1);
+  if constexpr (!kProd) {   // with a producer wave, it issues every tile copy
+    if (n_tiles > 0) {
+      prep_tile(0);
+      issue_quads(0, -1);
+    }
+    if (n_tiles > 1) {
+      prep_tile(1);
+      issue_quads(1, -1);
+    }
   }
 
   // ---- query operands: q split into two E4M3 terms hi + lo with a shared
@@ -658,10 +660,12 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
     // tile `it` landed in LDS (this wave's DMAs), then everyone's (barrier);
     // the barrier also retires every wave's reads of the buffer reused next
     asm volatile("" ::: "memory");
-    if (it + 1 < n_tiles) wait_vmcnt<C::NQ / kQStep>(); else wait_vmcnt<0>();
+    if constexpr (!kProd) {
+      if (it + 1 < n_tiles) wait_vmcnt<C::NQ / kQStep>(); else wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const bool refill = it + 2 < n_tiles;
+    const bool refill = !kProd && it + 2 < n_tiles;
     const int nbuf = buf == 0 ? 2 : buf - 1;
     if (refill) {
       prep_tile(it + 2);
@@ -827,14 +831,111 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, const Block& bk, 
   }
 }
 
+// The DMA producer of a workgroup (one extra wave, decode shape): it issues
+// every tile copy, so that the stalls of the per-CU limit on vector-memory
+// instructions in flight fall on it and not on the waves that compute.  It
+// copies the same 1 KB blocks the computing waves would (block (q, rg): 16
+// keys of row group rg, 64 bytes of each, lane l one key and one 16-byte
+// chunk), waits for a tile's copies before the tile's arrival barrier, and
+// meets every barrier the computing waves execute: one after the
+// descriptors, per tile the arrival, the score exchange, the tile max (four
+// dim parts) and the P exchange, and the denominator exchange after the
+// last tile.  A tile's 4 NQ copies go out in three parts, one after each
+// of the arrival, score-exchange and P-exchange barriers (spread over the
+// tile: c2 27.8 us, against 28.2 with two parts after the arrival and 29.4
+// with all of them).
+template <int DN, int DR, int ND>
+__device__ __forceinline__ void attn_producer(const AttnParams& p, const Block& bk, uint8_t* xs0, const int32_t* desc) {
+  using C = Cfg<DN, DR>;
+  constexpr int kN = 4 * C::NQ;            // copies per tile
+  static_assert(kN < 64, "a tile's copies fit the vmcnt range");
+  constexpr int kPer = (kN + 2) / 3;
+  const int lane = threadIdx.x & 63;
+  const int dcc = lane >> 4;
+  __syncthreads();   // the descriptors are visible
+  const int nkeys = bk.nkeys;
+  const int n_tiles = (nkeys + kAttnTile - 1) / kAttnTile;
+  const uint8_t* sn[4];
+  const uint8_t* sr[4];
+  auto prep = [&](int tile) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int key = 16 * rg + ((lane & 15) ^ (((rg ^ dcc) & 1) << 3));
+      const int s = tile * kAttnTile + key;
+      const int d = s < nkeys ? desc[s] : -1;
+      const uint8_t* nsrc = kZeroRow;
+      const uint8_t* rsrc = kZeroRow;
+      if (d >= 0) {
+        const size_t row = (size_t)(d & ~kSwaFlag);
+        if (d & kSwaFlag) {
+          nsrc = p.swa_nope + row * DN;
+          rsrc = reinterpret_cast<const uint8_t*>(p.swa_rope + row * DR);
+        } else {
+          nsrc = p.lat_nope + row * DN;
+          rsrc = reinterpret_cast<const uint8_t*>(p.lat_rope + row * DR);
+        }
+      }
+      sn[rg] = nsrc;
+      sr[rg] = rsrc;
+    }
+  };
+  auto issue = [&](int buf, int part) {
+    const uint32_t base = (uint32_t)(uintptr_t)(CSA_LDS uint8_t*)(xs0 + buf * C::TILE_BYTES);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      if (part >= 0 && i / kPer != part) continue;
+      const int q = i >> 2, rg = i & 3;
+      const int c = 4 * q + dcc;
+      const uint8_t* src;
+      if (4 * q < C::CHNP) {
+        src = (C::CHN == C::CHNP || c < C::CHN) ? sn[rg] + 16 * c : sn[rg];
+      } else {
+        const int cr = c - C::CHNP;
+        src = (C::CHR == C::CHRP || cr < C::CHR) ? sr[rg] + 16 * cr : sr[rg];
+      }
+      dma16(src, base + (uint32_t)(q * 4096 + rg * 1024));
+    }
+  };
+  if (n_tiles > 0) {
+    prep(0);
+    issue(0, -1);
+  }
+  if (n_tiles > 1) {
+    prep(1);
+    issue(1, -1);
+  }
+  int buf = 0;
+  for (int it = 0; it < n_tiles; ++it, buf = (buf + 1 == kNBuf) ? 0 : buf + 1) {
+    asm volatile("" ::: "memory");
+    if (it + 1 < n_tiles) wait_vmcnt<kN>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();   // arrival; the buffer refilled next is retired
+    asm volatile("" ::: "memory");
+    const bool refill = it + 2 < n_tiles;
+    const int nbuf = buf == 0 ? 2 : buf - 1;
+    if (refill) {
+      prep(it + 2);
+      issue(nbuf, 0);
+    }
+    __builtin_amdgcn_s_barrier();                 // score exchange
+    if (refill) issue(nbuf, 1);
+    if constexpr (ND == 4) __builtin_amdgcn_s_barrier();   // tile max
+    __builtin_amdgcn_s_barrier();                 // P exchange
+    if (refill) issue(nbuf, 2);
+  }
+  __builtin_amdgcn_s_barrier();   // denominator exchange
+}
+
 // HT = 16-head tiles per workgroup, ND = dim parts per head tile; one wave
 // per (tile, part), so ND * HT waves.  Few queries: HT = 2 with ND = 4 (eight
 // waves on 32 heads, two per SIMD, so that one wave's softmax runs while the
 // other's MFMAs do).  Enough (query, head group) pairs to fill the GPU
 // without splitting key ranges: HT = 4 with ND = 2 (each tile shared by 64
 // heads, again two waves per SIMD).
-template <int DN, int DR, int HT, int ND>
-__global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
+//
+// kProd: one more wave, the DMA producer (the decode shape, when the
+// workgroup does not select its own top-k).
+template <int DN, int DR, int HT, int ND, bool kProd>
+__global__ __launch_bounds__(64 * (ND * HT + (kProd ? 1 : 0)), 1) void attn_kernel(AttnParams p) {
   using C = Cfg<DN, DR>;
   // the tile ring (also the selection histograms of csa_topk_decode_attn
   // before the first tile, which need more than the small tiles' ring)
@@ -893,7 +994,7 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   // live in the tile ring and the indices in the score-exchange buffer,
   // which hold nothing yet.
   const int32_t* sel = nullptr;
-  if (p.scores) {
+  if (!kProd && p.scores) {
     using namespace topk_sel;
     constexpr int kThreads = 64 * ND * HT;
     constexpr int kSelSeg = kAttnSelMax / kThreads;
@@ -939,21 +1040,27 @@ __global__ __launch_bounds__(64 * ND * HT, 1) void attn_kernel(AttnParams p) {
   }
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __builtin_assume(wave >= 0 && wave < ND * HT);
+  __builtin_assume(wave >= 0 && wave < ND * HT + (kProd ? 1 : 0));
+  if constexpr (kProd) {
+    if (wave == ND * HT) {
+      attn_producer<DN, DR, ND>(p, bk, xs, desc);
+      return;
+    }
+  }
   if constexpr (ND == 4) {
     if (wave >= 3 * HT)
-      attn_wave<DN, DR, 3, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
+      attn_wave<DN, DR, 3, HT, ND, kProd>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else if (wave >= 2 * HT)
-      attn_wave<DN, DR, 2, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
+      attn_wave<DN, DR, 2, HT, ND, kProd>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
+      attn_wave<DN, DR, 1, HT, ND, kProd>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
+      attn_wave<DN, DR, 0, HT, ND, kProd>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
   } else {
     if (wave >= HT)
-      attn_wave<DN, DR, 1, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
+      attn_wave<DN, DR, 1, HT, ND, kProd>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
     else
-      attn_wave<DN, DR, 0, HT, ND>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
+      attn_wave<DN, DR, 0, HT, ND, kProd>(p, bk, xs, desc, sx, pxh, pxb, wave, sel);
   }
 }
 
@@ -1043,9 +1150,11 @@ hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
   const int blocks = (p.T >= 8 ? ((p.T + 7) / 8) * 8 : p.T) * nb;
   constexpr int kNd = Cfg<DN, DR>::NBLK == 4 ? 4 : 2;   // dim parts of the 32-head shape
   if (p.ht == 4)
-    hipLaunchKernelGGL((attn_kernel<DN, DR, 4, 2>), dim3(blocks), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<DN, DR, 4, 2, false>), dim3(blocks), dim3(512), 0, stream, p);
+  else if (p.scores)   // the selection in the prologue runs on the computing waves alone
+    hipLaunchKernelGGL((attn_kernel<DN, DR, 2, kNd, false>), dim3(blocks), dim3(64 * 2 * kNd), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_kernel<DN, DR, 2, kNd>), dim3(blocks), dim3(64 * 2 * kNd), 0, stream, p);
+    hipLaunchKernelGGL((attn_kernel<DN, DR, 2, kNd, true>), dim3(blocks), dim3(64 * (2 * kNd + 1)), 0, stream, p);
   hipError_t e = hipPeekAtLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   static_assert((DN + DR) / 4 <= 128, "one 128-thread team per (query, head)");
