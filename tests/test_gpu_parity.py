@@ -326,6 +326,11 @@ def _prefill_fused_case(case):
     if case == "k1024":
         spec = ci.Spec(name="prefill_k1024", kind="prefill", ctx_lens=[20000], T_prefill=50, k=1024)
         return ci.generate(spec, seed=184), [0, 49]
+    if case == "rows_shorter_than_k":
+        # every row sees fewer entries than k: all of them, then padding
+        spec = ci.Spec(name="prefill_short", kind="prefill", ctx_lens=[2000], T_prefill=40, k=1024,
+                       shuffle_pages=True)
+        return ci.generate(spec, seed=190), [0, 39]
     if case == "k_above_buffer":
         # k beyond the per-query candidate buffer: the one-query fused kernel
         spec = ci.Spec(name="prefill_k1500", kind="prefill", ctx_lens=[20000], T_prefill=24, k=1500)
@@ -358,8 +363,8 @@ def _prefill_fused_case(case):
     return dataclasses.replace(wl, k_idx=k_idx), [0, 63]
 
 
-@pytest.mark.parametrize("case", ["ragged_T70", "T16", "split_merge", "k1024", "k_above_buffer", "tiny_dims",
-                                  "all_tied", "five_values", "poisoned", "c4"])
+@pytest.mark.parametrize("case", ["ragged_T70", "T16", "split_merge", "k1024", "rows_shorter_than_k",
+                                  "k_above_buffer", "tiny_dims", "all_tied", "five_values", "poisoned", "c4"])
 def test_fused_index_topk_prefill_equals_two_calls(case):
     # many queries of one sequence: workgroups of queries share each key
     # tile and every query keeps a candidate buffer on chip; the indices are
@@ -387,6 +392,9 @@ def test_fused_index_topk_prefill_equals_two_calls(case):
     n_vis = two.n_vis.cpu().numpy()
     for t in range(0, wl.T, max(1, wl.T // 16)):
         P.check_topk_exact_on_gpu_scores(topk[t], scores[t][:n_vis[t]], wl.spec.k)
+    if case == "rows_shorter_than_k":
+        assert all(int(n_vis[t]) < wl.spec.k and (topk[t][:n_vis[t]] == np.arange(n_vis[t])).all()
+                   and (topk[t][n_vis[t]:] == -1).all() for t in range(wl.T))
     if case == "all_tied":
         for t in range(wl.T):
             K = min(wl.spec.k, int(n_vis[t]))
