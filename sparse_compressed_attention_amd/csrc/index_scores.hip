@@ -7,19 +7,21 @@
 // weighted ReLU over the heads ("weighted-ReLU MQA logits"), run on the
 // tensor units in FP8 over every visible compressed entry.
 //
-// Mapping on gfx950: one workgroup (4 waves) scores one query row over a
-// chunk of 256 entries; each wave owns 64 consecutive entries = 4 groups of
+// Mapping on gfx950: one workgroup (8 waves) scores one query row over a
+// chunk of 512 entries; each wave owns 64 consecutive entries = 4 groups of
 // 16.  Per group a wave runs one v_mfma 16x16x128 FP8 per 16 index heads:
 // A = the query's index heads (rows) x 128 dims; B = 16 entry keys x 128
 // dims, loaded straight from memory into the operand registers (each key
 // byte is used once, so no LDS staging).  The workgroup reads the query
-// operand once (one tile of 16 heads per wave) and shares it through LDS.
+// operand once (one tile of 16 heads per wave, waves 0-3) and shares it
+// through LDS.
 // The pages of the wave's groups come from one vector load (lane u fetches
 // group u's page id; a group of 16 never straddles a page because the page
 // size is a multiple of 16), then all of the wave's key loads are issued
 // before the first MFMA.  Short workgroups at four waves per SIMD keep 8 KB
 // in flight per wave and let the hardware rebalance ragged rows as
-// workgroups finish.  The ReLU, the head weights and the reduction over
+// workgroups finish.  Prefill chunks (many queries of one sequence) take the
+// many-query kernel below, and the fused indexer + top-k kernels follow it.  The ReLU, the head weights and the reduction over
 // heads stay in registers; the head reduction crosses the four 16-lane
 // groups with two permlane swaps.  The scan is HBM-bound (128 FLOP/byte).
 #include "csa_device.h"
