@@ -407,6 +407,35 @@ def test_fused_index_topk_prefill_equals_two_calls(case):
     say(f"  {case}: fused == two calls on {wl.T} rows; exact top-k sets vs oracle {exact}/{len(qs)}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_fused_index_topk_prefill_random_shapes(seed):
+    # seeded random prefill shapes (chunk length, context, k, page size,
+    # indexer heads and dims): the many-query fused call against the two calls
+    rng = np.random.default_rng(1900 + seed)
+    T = int(rng.integers(16, 160))
+    ctx = int(rng.integers(T + 64, 24000)) // 4 * 4
+    k = int(rng.choice([16, 64, 300, 512, 777, 1024]))
+    ps = int(rng.choice([16, 32, 64]))
+    H_I, D_I = [(64, 128), (40, 64), (24, 96), (8, 32)][int(rng.integers(0, 4))]
+    spec = ci.Spec(name=f"prefill_rand{seed}", kind="prefill", ctx_lens=[ctx], T_prefill=T, k=k, page_size=ps,
+                   H_I=H_I, D_I=D_I, H=8, D_nope=48, D_rope=16, W=32, shuffle_pages=bool(seed % 2))
+    say(f"case fused prefill random seed {seed}: T {T} ctx {ctx} k {k} page {ps} indexer {H_I}x{D_I}")
+    wl = ci.generate(spec, seed=1950 + seed)
+    d = to_device(wl, "cuda")
+    two = make_path(d)
+    fused = make_path(d, fused_topk=True)
+    two.run()
+    fused.topk.fill_(-7)
+    fused.run()
+    torch.cuda.synchronize()
+    assert torch.equal(two.topk, fused.topk)
+    assert torch.equal(two.n_vis, fused.n_vis)
+    assert torch.equal(two.out.view(torch.int16), fused.out.view(torch.int16))
+    topk, scores, n_vis = fused.topk.cpu().numpy(), two.scores.cpu().numpy(), two.n_vis.cpu().numpy()
+    for t in (0, T // 2, T - 1):
+        P.check_topk_exact_on_gpu_scores(topk[t], scores[t][:n_vis[t]], k)
+
+
 # --------------------------------------------------------------- MXFP4 indexer
 @pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "prefill_small", "tiny_dims_wide",
                                   "heads40_dims64", "heads24_dims96_prefill"])
