@@ -288,7 +288,9 @@ static_assert(kMqGroups % 4 == 0, "groups are reduced four at a time");
 // group holds its 16 code bytes in dwords 0-3 and its block's scale byte in
 // dword 4; the scaled MFMA reads only dwords 0-3 of an FP4 operand.
 //
-// kQ queries (waves) per workgroup.  kFused: the scores never leave the
+// kQ queries (waves) per workgroup.  The scores kernel runs two workgroups
+// per CU (64 KB of LDS each, registers for four waves per SIMD).  kFused:
+// one workgroup per CU; the scores never leave the
 // chip.  Every wave keeps a candidate buffer of (key, entry) pairs in LDS, in
 // entry order, and a threshold: an entry goes in only if its
 // order-preserving key is above the threshold (later entries are higher in
@@ -305,7 +307,7 @@ constexpr int kFtMqCap = 1792;   // candidate slots per wave (8 waves: 84 KB of 
 constexpr int kFtMqMaxK = 1024;   // largest k: a cut leaves room for at least one chunk
 static_assert(kFtMqCap - kMqChunk >= kFtMqMaxK, "a buffer cut to k has room for a chunk");
 template <bool kFp4, int kQ, bool kFused>
-__global__ __launch_bounds__(64 * kQ, kFused ? 1 : 2) void index_scores_mq_kernel(IndexParams p, TopkParams tp,
+__global__ __launch_bounds__(64 * kQ, kFused ? 1 : 4) void index_scores_mq_kernel(IndexParams p, TopkParams tp,
                                                                                 int n_split) {
   static_assert(!kFused || !kFp4, "fused indexer + top-k: E4M3 operands");
   constexpr int kMqGpw = kMqGroups / kQ;    // groups loaded per wave per chunk
@@ -567,20 +569,31 @@ __global__ __launch_bounds__(64 * kQ, kFused ? 1 : 2) void index_scores_mq_kerne
 #pragma unroll
       for (int w = 0; w < kQ; ++w) ok_mask |= okw[b][w];
       const int e_end = min(nv_own, e0 + kMqChunk);
-      // MFMAs of group u + 1 before the weighted ReLU of group u; one
-      // reduce-scatter per four groups (as in the one-query kernel)
-      v4f acc[2][4];
+      // Scores kernel: one accumulator set; the other waves of its SIMD (four
+      // per SIMD) hide the MFMA latency, and the registers a second set would
+      // take are what allow that occupancy.  Fused kernel (two waves per
+      // SIMD): the MFMAs of group u + 1 go before the weighted ReLU of group
+      // u, into a second set.  One reduce-scatter per four groups.
+      constexpr int kAcc = kFused ? 2 : 1;
+      v4f acc[kAcc][4];
       float xg[4];
       float sq[kMqGroups / 4];   // fused: entry e0 + 64 i + lane of the chunk
-      v8i kb = ks[b][lane];
-      mfmas(kb, acc[0]);
+      if constexpr (kFused) {
+        const v8i kb = ks[b][lane];
+        mfmas(kb, acc[0]);
+      }
 #pragma unroll
       for (int u = 0; u < kMqGroups; ++u) {
-        if (u + 1 < kMqGroups) {
-          kb = ks[b][(u + 1) * 64 + lane];
-          mfmas(kb, acc[(u + 1) & 1]);
+        if constexpr (kFused) {
+          if (u + 1 < kMqGroups) {
+            const v8i kb = ks[b][(u + 1) * 64 + lane];
+            mfmas(kb, acc[(u + 1) & 1]);
+          }
+        } else {
+          const v8i kb = ks[b][u * 64 + lane];
+          mfmas(kb, acc[0]);
         }
-        xg[u & 3] = wrelu16(acc[u & 1], wv);
+        xg[u & 3] = wrelu16(acc[u % kAcc], wv);
         if ((u & 3) == 3) {
           const float tot = reduce4_scatter(xg[0], xg[1], xg[2], xg[3]);
           const int ug = u - 3 + g;
