@@ -993,7 +993,18 @@ __global__ __launch_bounds__(64 * (ND * HT + (kProd ? 1 : 0)), 1) void attn_kern
   bk.sel_end = (bk.n_sel + kAttnTile - 1) & ~(kAttnTile - 1);
   const int n_slots = bk.sel_end + p.W;
   bk.kv0 = bk.split * p.per_split;
-  if (bk.split > 0 && bk.kv0 >= n_slots) return;   // empty split: the merge skips it
+  if (bk.split > 0 && bk.kv0 >= n_slots) {
+    // empty split: an empty state (M = -inf, L = 0), which the merge weighs
+    // by zero without reading the split's output
+    const int h = bk.hg * 16 * HT + (int)threadIdx.x;
+    if ((int)threadIdx.x < 16 * HT && h < p.H) {
+      constexpr int D = DN + DR;
+      float* dst = reinterpret_cast<float*>(p.part + (((size_t)bk.split * p.T + bk.t) * p.H + h) * part_row_bytes(D) + 2 * D);
+      dst[0] = -__builtin_inff();
+      dst[1] = 0.0f;
+    }
+    return;
+  }
   bk.nkeys = max(0, min(n_slots, bk.kv0 + p.per_split) - bk.kv0);
 
   // ---- top-k from the indexer scores (csa_topk_decode_attn): the
@@ -1074,71 +1085,71 @@ __global__ __launch_bounds__(64 * (ND * HT + (kProd ? 1 : 0)), 1) void attn_kern
 
 // Combines the per-split partial states (the split's output normalised by
 // its denominator, in BF16; running max in log2 units; denominator) of every
-// (query, head) into the output and lse.  128 threads per (query, head): the
-// split weights L_s exp2(M_s - M) are computed once into LDS (thread s owns
-// split s), then thread i sums dims [4 i, 4 i + 4) over the splits with
-// 8-byte loads.
+// (query, head) into the output and lse.  Every split leaves a state (an
+// empty split an empty one: M = -inf, L = 0), so the merge needs nothing
+// but the partials.  128 threads per (query, head): thread i loads every
+// split's (M, L) and dims [4 i, 4 i + 4) of every split's output at once
+// (one round trip for up to kMergeRegs splits, two passes beyond), then
+// weighs them in registers, the splits summed in order.
+constexpr int kMergeRegs = 16;
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  __shared__ float wgt[2][kAttnMaxSplits];
-  __shared__ float red[2][2][2];
   const int D = p.D_nope + p.D_rope;
   const size_t RB = part_row_bytes(D);
-  const int half = threadIdx.x >> 7;          // pair of this thread within the workgroup
+  const int pair = blockIdx.x * 2 + (threadIdx.x >> 7);   // (query, head) of this thread's team
   const int sub = threadIdx.x & 127;
-  const int wv = (threadIdx.x >> 6) & 1;      // wave within the pair
-  const int pair = blockIdx.x * 2 + half;
-  const bool pair_ok = pair < p.T * p.H;
-  const int t = pair_ok ? pair / p.H : 0;
-  const int h = pair_ok ? pair - t * p.H : 0;
-  const bool prefill = p.prefill_seq >= 0;
-  const int seq = prefill ? p.prefill_seq : t;
-  const int pos = p.q_pos[t];
-  const int nv = pos >= 0 ? max(0, min(pos / p.ratio_m, p.n_comp[seq])) : 0;
-  const int n_slots = (((p.topk || p.scores ? p.k : nv) + kAttnTile - 1) & ~(kAttnTile - 1)) + p.W;
-  const int used = max(1, min(p.n_splits, (n_slots + p.per_split - 1) / p.per_split));
+  if (pair >= p.T * p.H) return;
+  const int t = pair / p.H;
+  const int h = pair - t * p.H;
+  const int n = p.n_splits;
+  const int pos = p.inv_rope ? p.q_pos[t] : 0;
   const size_t pstride = (size_t)p.T * p.H * RB;   // one split (bytes)
   const uint8_t* row = p.part + ((size_t)t * p.H + h) * RB;
-
-  // split weights and the merged max / denominator
-  float m = -__builtin_inff(), l = 0.0f;
-  if (pair_ok && sub < used) {
-    const float2 ml = *reinterpret_cast<const float2*>(row + sub * pstride + 2 * D);
-    m = ml.x;
-    l = ml.y;
-  }
-  float mm = m;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
-  if ((threadIdx.x & 63) == 0) red[half][0][wv] = mm;
-  __syncthreads();
-  const float M = fmaxf(red[half][0][0], red[half][0][1]);
-  const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
-  const float a = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Ms);
-  float la = l * a;
-  if (sub < kAttnMaxSplits) wgt[half][sub] = la;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) la += __shfl_xor(la, off, 64);
-  if ((threadIdx.x & 63) == 0) red[half][1][wv] = la;
-  __syncthreads();
-  const float L = red[half][1][0] + red[half][1][1];
-  if (!pair_ok) return;
-  const float invL = L > 0.0f ? 1.0f / L : 0.0f;
   const int d0 = 4 * sub;
-  if (d0 < D) {
-    auto unpack = [](v2i w) -> v4f {
-      return (v4f){__uint_as_float((uint32_t)w[0] << 16), __uint_as_float((uint32_t)w[0] & 0xffff0000u),
-                   __uint_as_float((uint32_t)w[1] << 16), __uint_as_float((uint32_t)w[1] & 0xffff0000u)};
-    };
-    v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 4 <= used; s += 4) {
-      v2i v[4];
+  const bool dim_ok = d0 < D;
+  auto unpack = [](v2i w) -> v4f {
+    return (v4f){__uint_as_float((uint32_t)w[0] << 16), __uint_as_float((uint32_t)w[0] & 0xffff0000u),
+                 __uint_as_float((uint32_t)w[1] << 16), __uint_as_float((uint32_t)w[1] & 0xffff0000u)};
+  };
+  // weight of a split against the merged max Ms: L_s 2^(M_s - Ms), zero for
+  // an empty split (whose output row is never read into the sum)
+  auto weight = [](float2 ml, float Ms) -> float {
+    return ml.x == -__builtin_inff() ? 0.0f : ml.y * __builtin_amdgcn_exp2f(ml.x - Ms);
+  };
+  float M = -__builtin_inff(), L = 0.0f;
+  v4f acc = (v4f){0.f, 0.f, 0.f, 0.f};
+  if (n <= kMergeRegs) {
+    float2 ml[kMergeRegs];
+    v2i v[kMergeRegs];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const v2i*>(row + (s + j) * pstride + 2 * d0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc += unpack(v[j]) * wgt[half][s + j];
+    for (int s = 0; s < kMergeRegs; ++s) {
+      if (s < n) {
+        ml[s] = *reinterpret_cast<const float2*>(row + s * pstride + 2 * D);
+        v[s] = dim_ok ? *reinterpret_cast<const v2i*>(row + s * pstride + 2 * d0) : (v2i){0, 0};
+      }
     }
-    for (; s < used; ++s) acc += unpack(*reinterpret_cast<const v2i*>(row + s * pstride + 2 * d0)) * wgt[half][s];
+#pragma unroll
+    for (int s = 0; s < kMergeRegs; ++s)
+      if (s < n) M = fmaxf(M, ml[s].x);
+    const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
+#pragma unroll
+    for (int s = 0; s < kMergeRegs; ++s) {
+      if (s < n) {
+        const float w = weight(ml[s], Ms);
+        L += w;
+        if (w > 0.0f) acc += unpack(v[s]) * w;
+      }
+    }
+  } else {
+    for (int s = 0; s < n; ++s) M = fmaxf(M, reinterpret_cast<const float*>(row + s * pstride + 2 * D)[0]);
+    const float Ms = (M == -__builtin_inff()) ? 0.0f : M;
+    for (int s = 0; s < n; ++s) {
+      const float w = weight(*reinterpret_cast<const float2*>(row + s * pstride + 2 * D), Ms);
+      L += w;
+      if (w > 0.0f && dim_ok) acc += unpack(*reinterpret_cast<const v2i*>(row + s * pstride + 2 * d0)) * w;
+    }
+  }
+  const float invL = L > 0.0f ? 1.0f / L : 0.0f;
+  if (dim_ok) {
     if (d0 >= p.D_nope && p.inv_rope) {
       // inverse RoPE of rope pairs (d0 - D_nope) / 2 and the next one
       const int pr = (d0 - p.D_nope) >> 1;
