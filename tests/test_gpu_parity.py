@@ -826,6 +826,35 @@ def test_topk_all_equals_hca_mode():
         say(f"  query {t}: {int(nv[t])} visible, top-k vs HCA max|diff| {err:.2e}, min cos {cos:.6f}")
 
 
+def test_split_merge_ignores_stale_workspace():
+    # The merge reads every split's (max, denominator) and row: a split whose
+    # range lies past its query's slots must leave an empty state, so a
+    # workspace full of NaN bytes (stale data of earlier calls) changes
+    # nothing.  Two queries of very different length: most of the short
+    # one's splits are empty.
+    say("case split merge over a NaN-filled workspace")
+    spec = ci.small_spec(name="stale_ws", ctx_lens=[200000, 700], m=128, with_indexer=False)
+    wl = ci.generate(spec, seed=341)
+    s = wl.spec
+    d = to_device(wl, "cuda")
+    cache = csa.LatentCache(d.lat_nope, d.lat_rope, d.lat_scale, d.page_table, d.n_comp, s.m)
+    swa = csa.SwaRing(d.swa_nope, d.swa_rope, d.swa_scale, d.swa_pos)
+    max_keys = d.page_table.shape[1] * d.lat_nope.shape[1] + s.W
+    ws_bytes = csa.csa_attn_workspace_size(wl.T, s.H, s.D_nope, s.D_rope, max_keys)
+    assert ws_bytes > 0   # the key ranges are split
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.T, s.H, s.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((wl.T, s.H), dtype=torch.float32, device="cuda")
+    csa.csa_decode_attn(d.q, cache, None, 0, swa, d.q_pos, d.sink, s.sigma, out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    o = P.bf16_to_f64(out)
+    lv = lse.cpu().numpy().astype(np.float64)
+    for t in range(wl.T):
+        o_ref, l_ref = P.reference_attention_on(wl, t, None)
+        err, cos = P.check_attention(o[t], lv[t], o_ref, l_ref)
+        say(f"  query {t}: max|err| {err:.2e}, min cos {cos:.6f}")
+
+
 # --------------------------------------------------------------- top-k inside the attention
 @pytest.mark.parametrize("case", ["c0", "small_ragged", "many_sequences", "tiny_dims_wide", "poisoned", "c1", "c2",
                                   "k2048", "empty_rows"])
