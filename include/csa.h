@@ -320,7 +320,9 @@ int csa_topk_decode_attn(const float* scores, int64_t ld_scores,
  * device's array address once.  When the preferred split does not fit, the
  * call uses fewer splits; CSA_ERR_TOO_LARGE when even the minimum split's
  * partial results exceed the array.  Nothing in the array needs clearing:
- * every partial row the merge reads is written by the same call.  All calls
+ * every split's (max, denominator) state is written by the same call (an
+ * empty split's as empty), and the merge uses a split's row only when its
+ * state is not empty.  All calls
  * on one GPU share its array, which keeps the last call's contents, so
  * calls that overlap on one GPU (different streams, or graph replays in
  * flight together) race: serialise them. */
