@@ -350,6 +350,22 @@ def _prefill_fused_case(case):
         rows = wl.k_idx.reshape(-1, di)
         pick = rows[rng.integers(0, n, size=rows.shape[0]) if n > 1 else np.zeros(rows.shape[0], dtype=np.int64)]
         return dataclasses.replace(wl, k_idx=pick.reshape(P_, ps, di).copy()), []
+    if case == "ascending":
+        # key rows a growing multiple of one direction, the same within each
+        # 256-entry block: every block beats all the entries kept so far (the
+        # candidate buffers fill and are cut at every chunk) and ties exactly
+        # inside itself
+        spec = ci.Spec(name="prefill_ascending", kind="prefill", ctx_lens=[16000], T_prefill=33,
+                       shuffle_pages=True)
+        wl = ci.generate(spec, seed=191)
+        s = wl.spec
+        v = torch.from_numpy(wl.q_idx[0][0].copy()).view(torch.float8_e4m3fn).float().numpy()
+        v = v / np.abs(v).max() * 50.0
+        k_idx = wl.k_idx.copy()
+        for c in range(int(wl.n_comp[0])):
+            page = int(wl.page_table[0][c // s.page_size])
+            k_idx[page, c % s.page_size] = ci.e4m3_bytes((1.0 + 0.25 * (c // 256)) * v, 1.0)
+        return dataclasses.replace(wl, k_idx=k_idx), [0, 32]
     assert case == "poisoned"
     # own and future blocks made the strongest keys: never selected
     spec = ci.Spec(name="prefill_poisoned", kind="prefill", ctx_lens=[12000], T_prefill=64, shuffle_pages=True)
@@ -364,7 +380,8 @@ def _prefill_fused_case(case):
 
 
 @pytest.mark.parametrize("case", ["ragged_T70", "T16", "split_merge", "k1024", "rows_shorter_than_k",
-                                  "k_above_buffer", "tiny_dims", "all_tied", "five_values", "poisoned", "c4"])
+                                  "k_above_buffer", "tiny_dims", "all_tied", "five_values", "ascending", "poisoned",
+                                  "c4"])
 def test_fused_index_topk_prefill_equals_two_calls(case):
     # many queries of one sequence: workgroups of queries share each key
     # tile and every query keeps a candidate buffer on chip; the indices are
