@@ -277,7 +277,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // buffer); page ids run two chunks ahead.  LDS layout: the MFMA B operand of
 // group u (16 entries) for lane l at (u * 64 + l) * 32 bytes, so every lane
 // reads its 32 bytes contiguously.
-constexpr int kMqQ = 8;
+constexpr int kMqQ = 16;
 constexpr int kMqGroups = 16;
 constexpr int kMqChunk = 16 * kMqGroups;
 static_assert(kMqGroups % kMqQ == 0, "groups split evenly over the waves");
@@ -288,10 +288,10 @@ static_assert(kMqGroups % 4 == 0, "groups are reduced four at a time");
 // group holds its 16 code bytes in dwords 0-3 and its block's scale byte in
 // dword 4; the scaled MFMA reads only dwords 0-3 of an FP4 operand.
 //
-// kQ queries (waves) per workgroup.  The scores kernel runs two workgroups
-// per CU (64 KB of LDS each, registers for four waves per SIMD).  kFused:
-// one workgroup per CU; the scores never leave the
-// chip.  Every wave keeps a candidate buffer of (key, entry) pairs in LDS, in
+// kQ queries (waves) per workgroup.  The scores kernel runs one 16-wave
+// workgroup per CU (64 KB of LDS, registers for four waves per SIMD), so a
+// staged chunk serves 16 queries.  kFused: one 8-wave workgroup per CU; the
+// scores never leave the chip.  Every wave keeps a candidate buffer of (key, entry) pairs in LDS, in
 // entry order, and a threshold: an entry goes in only if its
 // order-preserving key is above the threshold (later entries are higher in
 // index, so one tied with the threshold ranks below every kept one).  When a
@@ -839,9 +839,9 @@ hipError_t launch_index_scores(const IndexParams& p_in, hipStream_t stream) {
     p.n_chunks = (int)std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
     const int64_t n_qb = (p.T + kMqQ - 1) / kMqQ;
     const int64_t span_ch = std::max<int64_t>(1, (span + kMqChunk - 1) / kMqChunk);
-    // about 512 workgroups (at 152 registers a CU holds one at a time), parts
-    // of at least 4 chunks
-    const int n_split = (int)std::max<int64_t>(1, std::min<int64_t>((512 + n_qb - 1) / n_qb, span_ch / 4));
+    // about 256 workgroups, one per CU (a 16-wave workgroup fills the four
+    // waves per SIMD its registers allow), parts of at least 4 chunks
+    const int n_split = (int)std::max<int64_t>(1, std::min<int64_t>((256 + n_qb - 1) / n_qb, span_ch / 4));
     const TopkParams none{};
     if (p.fp4)
       hipLaunchKernelGGL((index_scores_mq_kernel<true, kMqQ, false>), dim3((unsigned)(n_qb * n_split)),
