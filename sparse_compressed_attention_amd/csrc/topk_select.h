@@ -27,6 +27,32 @@ struct TopkShared {
   uint32_t red[2][kWaves];
 };
 
+// Wave-wide inclusive scans on DPP lane moves (VALU, no LDS round trip):
+// shifts by 1, 2, 4 and 8 within each row of 16 lanes (a lane with no
+// source adds 0), then the last lane of row 0 added into row 1 and of row 2
+// into row 3 (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31).
+// Lane 63 ends with the whole wave's result.
+__device__ __forceinline__ int wave_inclusive_add(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+// Largest value over the wave (unsigned; a lane with no source takes 0,
+// which never exceeds its own value)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
 // the sum of all.  Contains a barrier: every thread must call it, and two
 // calls must be separated by another barrier (the per-wave sums are reused).
@@ -34,12 +60,7 @@ template <int BLOCK>
 __device__ int block_exclusive_scan(int v, TopkShared<BLOCK>& sh, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_inclusive_add(v);
   if (lane == 63) sh.wsum[wave] = x;
   __syncthreads();
   int before = 0, tot = 0;
@@ -78,11 +99,8 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
       kmax = max(kmax, key[j]);
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
-  }
+  kmin = ~wave_max_u32(~kmin);
+  kmax = wave_max_u32(kmax);
   if (lane == 0) {
     sh.red[0][wave] = kmin;
     sh.red[1][wave] = kmax;
