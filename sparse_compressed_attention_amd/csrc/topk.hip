@@ -36,7 +36,9 @@ namespace {
 
 using namespace topk_sel;
 
-// (launch bounds: six 512-thread workgroups per CU when registers allow)
+// (launch bounds: at least six waves per SIMD, three 512-thread workgroups
+// per CU; at 32 keys per thread that caps a wave at 80 registers, and the
+// few it spills cost less than the lost occupancy would)
 template <int BLOCK, int SEG>
 __global__ __launch_bounds__(BLOCK, 6) void topk_chunk_kernel(TopkParams p) {
   __shared__ TopkShared<BLOCK> sh;
