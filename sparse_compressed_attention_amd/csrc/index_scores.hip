@@ -246,27 +246,6 @@ __global__ __launch_bounds__(64 * kWaves, kOcc) void index_scores_kernel(IndexPa
   }
 }
 
-// Minimum / maximum over the wave: rotations within each row of 16 lanes
-// (DPP row_ror 8, 4, 2, 1), then the four rows through readlane.
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));
-  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
-  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
-  return min(a, b);
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
-  return max(a, b);
-}
-
 // ---- many queries of one sequence (prefill) -----------------------------
 // All queries scan the same compressed keys, so a workgroup of kMqQ waves
 // takes kMqQ queries (one per wave) and walks the whole key range in chunks
@@ -415,8 +394,8 @@ __global__ __launch_bounds__(64 * kQ, kFused ? 1 : 4) void index_scores_mq_kerne
       vmin = v ? min(vmin, kr[q]) : vmin;
       vmax = v ? max(vmax, kr[q]) : vmax;
     }
-    vmin = wave_min_u32(vmin);
-    vmax = wave_max_u32(vmax);
+    vmin = topk_sel::wave_min_u32(vmin);
+    vmax = topk_sel::wave_max_u32(vmax);
     auto count_above = [&](uint32_t x) {
       int n = 0;
 #pragma unroll

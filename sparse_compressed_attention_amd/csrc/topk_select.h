@@ -52,6 +52,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
+// Smallest value over the wave (through the largest complement)
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
 // the sum of all.  Contains a barrier: every thread must call it, and two
@@ -99,7 +101,7 @@ __device__ Sel radix_select(const uint32_t (&key)[SEG], uint32_t valid, int K, T
       kmax = max(kmax, key[j]);
     }
   }
-  kmin = ~wave_max_u32(~kmin);
+  kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if (lane == 0) {
     sh.red[0][wave] = kmin;
