@@ -13,7 +13,8 @@
 //    cache (no Python loop, no BF16 materialisation); E4: (o, lse); E5: batch
 //    in the grid.
 //
-// Mapping on gfx950 (eight waves per workgroup, two per SIMD):
+// Mapping on gfx950 (eight computing waves per workgroup, two per SIMD; in
+// the decode shape a ninth wave only issues the tile copies):
 //  * a workgroup owns one query, HT x 16 heads and a range of key slots (the
 //    range is split over workgroups only when there are few queries);
 //  * wave (ht, dp): heads [16 ht, 16 ht + 16) of the group and dim part dp of
@@ -56,7 +57,8 @@
 //    from compressed entries to window rows); X^T comes from the same LDS tile through
 //    ds_read_b64_tr_b8 (two reads per 16 dims, used for both terms).  Rope
 //    dims use ds_read_b64_tr_b16 and v_mfma 16x16x32 BF16 with P in BF16.
-//    P never leaves registers.
+//    Each dim part exponentiates and packs P for its own 16-key subtiles
+//    only, and the parts swap those through LDS.
 #include <mutex>
 
 #include "csa_device.h"
