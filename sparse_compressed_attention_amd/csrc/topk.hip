@@ -18,8 +18,9 @@
 //    integer atomics, finds the digit with a workgroup prefix sum over the
 //    bins, and stops as soon as the selected bin holds exactly the keys still
 //    needed;
-//  * an ordered compaction (two workgroup prefix sums over the contiguous
-//    per-thread segments) emits the chunk's selection in ascending index
+//  * an ordered compaction (one workgroup prefix sum over the contiguous
+//    per-thread segments, of the counts above and equal to the threshold
+//    packed in one word) emits the chunk's selection in ascending index
 //    order -- the final answer when the row fits one chunk, else the chunk's
 //    candidates (key, index);
 //  * stage 2 (long rows only): one workgroup per row repeats the selection
