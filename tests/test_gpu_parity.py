@@ -137,6 +137,16 @@ def test_prefill_hca_mode(T):
     say(f"  max|err| {worst[0]:.3e} min cos {worst[1]:.6f}")
 
 
+def test_prefill_indexer_split_key_range():
+    # 40 queries = query blocks of 16, 16 and 8 (ragged) in the many-query
+    # scores kernel, whose key range (10250 entries, 41 chunks of 256) is
+    # cut into ten parts of four or five chunks; scores compared element by
+    # element with the oracle on queries at both ends of every block
+    say("case prefill indexer, split key range, ragged query block")
+    spec = ci.Spec(name="prefill_split_40", kind="prefill", ctx_lens=[41000], T_prefill=40)
+    check_full(ci.generate(spec, seed=127), queries=[0, 15, 16, 31, 32, 39])
+
+
 def test_prefill_64_head_workgroups():
     # 160 queries x 2 groups of 64 heads fill the GPU without splitting the
     # key range, so the launch uses 64-head (8-wave) workgroups
